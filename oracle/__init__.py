@@ -1,0 +1,185 @@
+"""CPU fp64 oracle for causal scaled dot-product attention (test infrastructure).
+
+Only the test suite, the smoke check and the bench's CPU-baseline leg may
+import this package.  The HIP library never loads it, and it never loads the
+HIP library: the two share no code.  The arithmetic lives in
+``attn_oracle.c`` (plain C, double precision, POSIX threads); this module only
+compiles it with gcc and marshals numpy arrays.
+
+Functions and the passages they follow (four web pages on attention
+profiling; each function's C counterpart states the definition it writes out):
+
+* ``attn_fwd``   -- softmax(scale * q k^T + causal mask) v and the per-row
+  log-sum-exp: the formula in the ainews.cool "technical deep-dive", with the
+  five-step causal pipeline of the Hugging Face article's "Naive Attention"
+  section (insight.aitobox.com rendering).
+* ``qk_scores``  -- step 1 of that pipeline (q k^T, unscaled).
+* ``masked_softmax`` -- steps 2-4 (scale, mask with -inf, softmax).
+* ``pv``         -- step 5 (attn v).
+
+Every function is pinned by tests in ``tests/test_oracle_pins.py`` against
+closed forms, invariants, hand-derived fixtures and independent library
+routines; see that file for which pin covers which part.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+HERE = Path(__file__).resolve().parent
+SRC = HERE / "attn_oracle.c"
+LIB = HERE / "liboracle.so"
+
+_i64 = ctypes.c_int64
+_ptr = ctypes.c_void_p
+
+
+def compile_oracle(out: Path = LIB, plant: int = 0) -> Path:
+    """Compile the oracle with gcc.  ``plant`` selects a deliberate-mistake
+    variant (tests only); 0 is the real oracle."""
+    out = Path(out)
+    out.parent.mkdir(parents=True, exist_ok=True)
+    tmp = out.with_name(out.name + f".tmp{os.getpid()}")
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+           f"-DORACLE_PLANT={int(plant)}", str(SRC), "-o", str(tmp), "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, path: Path = LIB):
+        path = Path(path)
+        if not path.exists():
+            compile_oracle(path)
+        self.path = path
+        self.lib = ctypes.CDLL(str(path))
+        L = self.lib
+        L.oracle_attn_fwd_rows.restype = ctypes.c_int
+        L.oracle_attn_fwd_rows.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64,
+                                           ctypes.c_double, ctypes.c_int, _ptr, _i64, _ptr, _ptr,
+                                           ctypes.c_int]
+        L.oracle_qk_scores_rows.restype = ctypes.c_int
+        L.oracle_qk_scores_rows.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _ptr, _i64,
+                                            _ptr, ctypes.c_int]
+        L.oracle_masked_softmax_rows.restype = ctypes.c_int
+        L.oracle_masked_softmax_rows.argtypes = [_ptr, _i64, _i64, _i64, ctypes.c_double,
+                                                 ctypes.c_int, _ptr, _i64, _ptr, _ptr, ctypes.c_int]
+        L.oracle_pv_rows.restype = ctypes.c_int
+        L.oracle_pv_rows.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _ptr, _i64, _ptr,
+                                     ctypes.c_int]
+        L.oracle_plant_id.restype = ctypes.c_int
+        L.oracle_plant_id.argtypes = []
+
+    @property
+    def plant(self) -> int:
+        return int(self.lib.oracle_plant_id())
+
+    # -- helpers -----------------------------------------------------------
+    @staticmethod
+    def _f32(x) -> np.ndarray:
+        a = np.ascontiguousarray(x, dtype=np.float32)
+        return a
+
+    @staticmethod
+    def _rows(rows, total: int) -> np.ndarray:
+        if rows is None:
+            return np.arange(total, dtype=np.int64)
+        return np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+
+    @staticmethod
+    def _threads(nthreads):
+        return int(nthreads) if nthreads else (os.cpu_count() or 1)
+
+    @staticmethod
+    def _check(rc: int, name: str):
+        if rc != 0:
+            raise RuntimeError(f"{name} failed with code {rc}")
+
+    # -- attention forward --------------------------------------------------
+    def attn_fwd(self, q, k, v, scale: float, causal: bool, rows=None, nthreads=None):
+        """out, lse for q ``[B,Hq,S,D]``, k/v ``[B,Hkv,S,D]``.
+
+        With ``rows=None`` returns out ``[B,Hq,S,D]`` and lse ``[B,Hq,S]``;
+        otherwise ``rows`` indexes the flattened ``[B,Hq,S]`` row space and
+        out is ``[len(rows), D]``, lse ``[len(rows)]``.
+        """
+        q, k, v = self._f32(q), self._f32(k), self._f32(v)
+        B, Hq, S, D = q.shape
+        Hkv = k.shape[1]
+        assert k.shape == (B, Hkv, S, D) and v.shape == k.shape
+        r = self._rows(rows, B * Hq * S)
+        out = np.empty((r.size, D), dtype=np.float64)
+        lse = np.empty((r.size,), dtype=np.float64)
+        rc = self.lib.oracle_attn_fwd_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                           B, Hq, Hkv, S, D, float(scale), int(bool(causal)),
+                                           r.ctypes.data, r.size, out.ctypes.data,
+                                           lse.ctypes.data, self._threads(nthreads))
+        self._check(rc, "oracle_attn_fwd_rows")
+        if rows is None:
+            return out.reshape(B, Hq, S, D), lse.reshape(B, Hq, S)
+        return out, lse
+
+    # -- unfused steps ------------------------------------------------------
+    def qk_scores(self, q, k, rows=None, nthreads=None):
+        """Unscaled scores q k^T: ``[B,Hq,S,S]`` (or ``[len(rows), S]``)."""
+        q, k = self._f32(q), self._f32(k)
+        B, Hq, S, D = q.shape
+        Hkv = k.shape[1]
+        assert k.shape == (B, Hkv, S, D)
+        r = self._rows(rows, B * Hq * S)
+        out = np.empty((r.size, S), dtype=np.float64)
+        rc = self.lib.oracle_qk_scores_rows(q.ctypes.data, k.ctypes.data, B, Hq, Hkv, S, D,
+                                            r.ctypes.data, r.size, out.ctypes.data,
+                                            self._threads(nthreads))
+        self._check(rc, "oracle_qk_scores_rows")
+        return out.reshape(B, Hq, S, S) if rows is None else out
+
+    def masked_softmax(self, scores, scale: float, causal: bool, rows=None, nthreads=None):
+        """p, lse from fp32 scores ``[B,H,S,S]`` (or per listed row)."""
+        x = self._f32(scores)
+        B, H, S, S2 = x.shape
+        assert S == S2
+        r = self._rows(rows, B * H * S)
+        p = np.empty((r.size, S), dtype=np.float64)
+        lse = np.empty((r.size,), dtype=np.float64)
+        rc = self.lib.oracle_masked_softmax_rows(x.ctypes.data, B, H, S, float(scale),
+                                                 int(bool(causal)), r.ctypes.data, r.size,
+                                                 p.ctypes.data, lse.ctypes.data,
+                                                 self._threads(nthreads))
+        self._check(rc, "oracle_masked_softmax_rows")
+        if rows is None:
+            return p.reshape(B, H, S, S), lse.reshape(B, H, S)
+        return p, lse
+
+    def pv(self, p, v, rows=None, nthreads=None):
+        """out = p v for p ``[B,Hq,S,S]``, v ``[B,Hkv,S,D]``."""
+        p, v = self._f32(p), self._f32(v)
+        B, Hq, S, S2 = p.shape
+        Hkv, D = v.shape[1], v.shape[3]
+        assert S == S2 and v.shape == (B, Hkv, S, D)
+        r = self._rows(rows, B * Hq * S)
+        out = np.empty((r.size, D), dtype=np.float64)
+        rc = self.lib.oracle_pv_rows(p.ctypes.data, v.ctypes.data, B, Hq, Hkv, S, D,
+                                     r.ctypes.data, r.size, out.ctypes.data,
+                                     self._threads(nthreads))
+        self._check(rc, "oracle_pv_rows")
+        return out.reshape(B, Hq, S, D) if rows is None else out
+
+
+_DEFAULT = None
+
+
+def default() -> Oracle:
+    """The real (unplanted) oracle, compiled on first use if needed."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle(LIB)
+        assert _DEFAULT.plant == 0
+    return _DEFAULT

@@ -1,0 +1,405 @@
+/*
+ * attn_oracle.c -- plain, slow, fp64 CPU oracle for causal scaled dot-product
+ * attention and for the three steps of the unfused pipeline.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the bench's CPU
+ * baseline leg use it.  It shares no code with the HIP library.
+ *
+ * What it computes (sources are the four web pages on attention profiling):
+ *   - The attention formula softmax(Q K^T / sqrt(d_k)) V, as stated in the
+ *     "technical deep-dive" of the ainews.cool AttentionProfiler article.
+ *   - The five-step causal pipeline of the Hugging Face "Profiling in PyTorch
+ *     (Part 3)" rendering on insight.aitobox.com, section "Naive Attention":
+ *     (1) scores = q k^T, (2) scores * scale, (3) masked_fill(mask, -inf),
+ *     (4) softmax over the key axis, (5) attn v.  The same list appears in the
+ *     chaosnode.de summary, section "Attention unter der Lupe".
+ *   - The scale 1/sqrt(head_dim) of the NaiveCausalAttention class in that same
+ *     section; here scale is an explicit argument.
+ *   - Layout [B, H, S, D], D fastest, from the naive_attention comment in
+ *     section 1 of the ai-manual.ru tutorial.
+ *
+ * Readings where the pages leave a step open:
+ *   - mask: key j is masked for query i when j > i (square S_q = S_k = S);
+ *     masked logits are exactly -inf, so their weight is exactly 0.  The
+ *     masked keys are therefore left out of the max and the sum.
+ *   - grouped-query attention: query head h reads key/value head
+ *     h / (Hq / Hkv) (contiguous groups); Hq must be a multiple of Hkv.
+ *   - lse (log-sum-exp of a row, not on the pages): ln(sum_j exp(s_ij)) over
+ *     the unmasked keys, with s already scaled.
+ *   - a row with no unmasked key cannot occur (key i is always visible to
+ *     query i); if it ever did, out = 0 and lse = -inf, like the "safe
+ *     softmax" of the math backend described in the SDPA section of the
+ *     Hugging Face article.
+ *
+ * Arithmetic: every product and sum is in double; inputs are float32 arrays
+ * holding the exact values the GPU sees (bf16 values are exact in float32).
+ * Work is split over rows (b, h, i) between POSIX threads.
+ *
+ * Mutation hooks: when compiled with -DORACLE_PLANT=<n> the oracle carries a
+ * deliberate mistake (see the PLANT blocks).  The test suite builds those
+ * variants to check that its pins catch each kind of mistake.  The normal
+ * build defines nothing and carries none of them.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdatomic.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORACLE_PLANT
+#define ORACLE_PLANT 0
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* shape and row bookkeeping                                                */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int64_t B, Hq, Hkv, S, D;
+} shape_t;
+
+/* Row r of the flattened [B, Hq, S] index space -> (b, h, i). */
+static void split_row(const shape_t* sh, int64_t r, int64_t* b, int64_t* h, int64_t* i) {
+    *i = r % sh->S;
+    int64_t bh = r / sh->S;
+    *h = bh % sh->Hq;
+    *b = bh / sh->Hq;
+}
+
+/* Key/value head read by query head h (contiguous GQA groups). */
+static int64_t kv_head(const shape_t* sh, int64_t h) {
+#if ORACLE_PLANT == 5
+    return h % sh->Hkv; /* planted: strided instead of contiguous groups */
+#else
+    return h / (sh->Hq / sh->Hkv);
+#endif
+}
+
+/* Last visible key for query i: i when causal (mask j > i), S-1 otherwise. */
+static int64_t last_key(const shape_t* sh, int64_t i, int causal) {
+#if ORACLE_PLANT == 3
+    if (causal) return (i + 1 < sh->S) ? i + 1 : i; /* planted: off-by-one mask */
+#endif
+    return causal ? i : sh->S - 1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* work distribution                                                        */
+/* ------------------------------------------------------------------------ */
+
+typedef void (*row_fn)(void* ctx, int64_t n, double* scratch);
+
+typedef struct {
+    row_fn fn;
+    void* ctx;
+    int64_t nrows;
+    int64_t scratch_len;
+    atomic_llong next;
+    atomic_int failed;
+} pool_t;
+
+static void* pool_worker(void* arg) {
+    pool_t* p = (pool_t*)arg;
+    double* scratch = (double*)malloc((size_t)(p->scratch_len > 0 ? p->scratch_len : 1) * sizeof(double));
+    if (!scratch) {
+        atomic_store(&p->failed, 1);
+        return NULL;
+    }
+    for (;;) {
+        int64_t n = atomic_fetch_add(&p->next, 1);
+        if (n >= p->nrows) break;
+        p->fn(p->ctx, n, scratch);
+    }
+    free(scratch);
+    return NULL;
+}
+
+/* Runs fn(ctx, n, scratch) for n in [0, nrows) on nthreads threads. */
+static int run_rows(row_fn fn, void* ctx, int64_t nrows, int64_t scratch_len, int nthreads) {
+    pool_t p;
+    p.fn = fn;
+    p.ctx = ctx;
+    p.nrows = nrows;
+    p.scratch_len = scratch_len;
+    atomic_init(&p.next, 0);
+    atomic_init(&p.failed, 0);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 1024) nthreads = 1024;
+    if ((int64_t)nthreads > nrows) nthreads = (int)(nrows > 0 ? nrows : 1);
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!th) return -1;
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, pool_worker, &p) != 0) break;
+        started = t;
+    }
+    pool_worker(&p);
+    for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+    free(th);
+    return atomic_load(&p.failed) ? -1 : 0;
+}
+
+static int check_shape(const shape_t* sh) {
+    if (sh->B < 1 || sh->Hq < 1 || sh->Hkv < 1 || sh->S < 1 || sh->D < 1) return -2;
+    if (sh->Hq % sh->Hkv != 0) return -2;
+    return 0;
+}
+
+static int check_rows(const shape_t* sh, const int64_t* rows, int64_t nrows) {
+    int64_t total = sh->B * sh->Hq * sh->S;
+    for (int64_t n = 0; n < nrows; ++n)
+        if (rows[n] < 0 || rows[n] >= total) return -3;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* attention, one row at a time (the definition written out)                */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const float *q, *k, *v;
+    shape_t sh;
+    double scale;
+    int causal;
+    const int64_t* rows;
+    double *out, *lse;
+} attn_ctx;
+
+/*
+ * For query row (b, h, i):
+ *   s_j   = scale * sum_d q[b,h,i,d] k[b,g,j,d]          j in J(i)
+ *   m     = max_j s_j
+ *   l     = sum_j exp(s_j - m)
+ *   out_d = sum_j exp(s_j - m) v[b,g,j,d] / l
+ *   lse   = m + ln l
+ * with g the key/value head of h and J(i) = {0..i} (causal) or {0..S-1}.
+ * Subtracting m changes nothing mathematically; it only keeps exp finite.
+ */
+static void attn_row(void* vctx, int64_t n, double* s) {
+    const attn_ctx* c = (const attn_ctx*)vctx;
+    const shape_t* sh = &c->sh;
+    int64_t b, h, i;
+    split_row(sh, c->rows[n], &b, &h, &i);
+    const int64_t g = kv_head(sh, h);
+    const int64_t S = sh->S, D = sh->D;
+    const float* qi = c->q + ((b * sh->Hq + h) * S + i) * D;
+    const float* kb = c->k + (b * sh->Hkv + g) * S * D;
+    const float* vb = c->v + (b * sh->Hkv + g) * S * D;
+    double* o = c->out + n * D;
+    const int64_t jl = last_key(sh, i, c->causal);
+
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= jl; ++j) {
+        const float* kj = kb + j * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+#if ORACLE_PLANT == 2
+            dot += (double)qi[d] * (double)kb[d * S + j]; /* planted: K read transposed */
+#else
+            dot += (double)qi[d] * (double)kj[d];
+#endif
+        }
+#if ORACLE_PLANT == 1
+        s[j] = dot; /* planted: scale dropped */
+#else
+        s[j] = c->scale * dot;
+#endif
+        if (s[j] > m) m = s[j];
+    }
+    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+    if (jl < 0 || m == -INFINITY) { /* no visible key: unreachable, see header */
+        c->lse[n] = -INFINITY;
+        return;
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j <= jl; ++j) {
+#if ORACLE_PLANT == 4
+        const double w = exp(m - s[j]); /* planted: sign flipped in the exponent */
+#else
+        const double w = exp(s[j] - m);
+#endif
+        l += w;
+        const float* vj = vb + j * D;
+        for (int64_t d = 0; d < D; ++d) o[d] += w * (double)vj[d];
+    }
+    for (int64_t d = 0; d < D; ++d) {
+#if ORACLE_PLANT == 6
+        (void)l; /* planted: normalisation dropped */
+#else
+        o[d] /= l;
+#endif
+    }
+#if ORACLE_PLANT == 7
+    c->lse[n] = m + log2(l); /* planted: wrong logarithm base */
+#else
+    c->lse[n] = m + log(l);
+#endif
+}
+
+/*
+ * Attention forward for the listed rows.  rows[n] indexes the flattened
+ * [B, Hq, S] row space; out is [nrows, D], lse is [nrows].
+ * q is [B,Hq,S,D], k and v are [B,Hkv,S,D], all float32, contiguous.
+ * Returns 0, or a negative code on a bad shape (-2), bad row (-3) or
+ * allocation failure (-1).
+ */
+int oracle_attn_fwd_rows(const float* q, const float* k, const float* v,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t S, int64_t D,
+                         double scale, int causal,
+                         const int64_t* rows, int64_t nrows,
+                         double* out, double* lse, int nthreads) {
+    attn_ctx c;
+    c.q = q; c.k = k; c.v = v;
+    c.sh.B = B; c.sh.Hq = Hq; c.sh.Hkv = Hkv; c.sh.S = S; c.sh.D = D;
+    c.scale = scale;
+    c.causal = causal ? 1 : 0;
+    c.rows = rows;
+    c.out = out;
+    c.lse = lse;
+    int rc = check_shape(&c.sh);
+    if (rc) return rc;
+    rc = check_rows(&c.sh, rows, nrows);
+    if (rc) return rc;
+    return run_rows(attn_row, &c, nrows, S, nthreads);
+}
+
+/* ------------------------------------------------------------------------ */
+/* the unfused pipeline, step by step                                       */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const float *a, *b;
+    shape_t sh;
+    double scale;
+    int causal;
+    const int64_t* rows;
+    double *out, *lse;
+} step_ctx;
+
+/* Step 1 for one row: scores[b,h,i,j] = sum_d q[b,h,i,d] k[b,g,j,d], all j. */
+static void qk_row(void* vctx, int64_t n, double* unused) {
+    (void)unused;
+    const step_ctx* c = (const step_ctx*)vctx;
+    const shape_t* sh = &c->sh;
+    int64_t b, h, i;
+    split_row(sh, c->rows[n], &b, &h, &i);
+    const int64_t g = kv_head(sh, h);
+    const int64_t S = sh->S, D = sh->D;
+    const float* qi = c->a + ((b * sh->Hq + h) * S + i) * D;
+    const float* kb = c->b + (b * sh->Hkv + g) * S * D;
+    double* o = c->out + n * S;
+    for (int64_t j = 0; j < S; ++j) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += (double)qi[d] * (double)kb[j * D + d];
+        o[j] = dot;
+    }
+}
+
+/* Unscaled scores q k^T for the listed rows; out is [nrows, S]. */
+int oracle_qk_scores_rows(const float* q, const float* k,
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t S, int64_t D,
+                          const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+    step_ctx c;
+    memset(&c, 0, sizeof c);
+    c.a = q; c.b = k;
+    c.sh.B = B; c.sh.Hq = Hq; c.sh.Hkv = Hkv; c.sh.S = S; c.sh.D = D;
+    c.rows = rows;
+    c.out = out;
+    int rc = check_shape(&c.sh);
+    if (rc) return rc;
+    rc = check_rows(&c.sh, rows, nrows);
+    if (rc) return rc;
+    return run_rows(qk_row, &c, nrows, 0, nthreads);
+}
+
+/*
+ * Steps 2-4 for one row of an [B,H,S,S] score matrix: t_j = scale * x_j;
+ * t_j = -inf for masked j; p_j = exp(t_j - max t) / sum exp(t - max t).
+ * Masked entries get p = 0 exactly.  lse = max t + ln(sum exp(t - max t)).
+ */
+static void softmax_row(void* vctx, int64_t n, double* t) {
+    const step_ctx* c = (const step_ctx*)vctx;
+    const shape_t* sh = &c->sh;
+    int64_t b, h, i;
+    split_row(sh, c->rows[n], &b, &h, &i);
+    const int64_t S = sh->S;
+    const float* x = c->a + ((b * sh->Hq + h) * S + i) * S;
+    double* p = c->out + n * S;
+    const int64_t jl = last_key(sh, i, c->causal);
+    double m = -INFINITY;
+    for (int64_t j = 0; j < S; ++j) {
+        t[j] = (j <= jl) ? c->scale * (double)x[j] : -INFINITY;
+        if (t[j] > m) m = t[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < S; ++j) {
+        p[j] = (j <= jl) ? exp(t[j] - m) : 0.0;
+        l += p[j];
+    }
+    for (int64_t j = 0; j < S; ++j) p[j] /= l;
+    if (c->lse) c->lse[n] = m + log(l);
+}
+
+/* Masked row softmax of fp32 scores [B,H,S,S] for the listed rows (H = Hq);
+ * p is [nrows, S]; lse is [nrows] or NULL. */
+int oracle_masked_softmax_rows(const float* scores,
+                               int64_t B, int64_t H, int64_t S,
+                               double scale, int causal,
+                               const int64_t* rows, int64_t nrows,
+                               double* p, double* lse, int nthreads) {
+    step_ctx c;
+    memset(&c, 0, sizeof c);
+    c.a = scores;
+    c.sh.B = B; c.sh.Hq = H; c.sh.Hkv = H; c.sh.S = S; c.sh.D = 1;
+    c.scale = scale;
+    c.causal = causal ? 1 : 0;
+    c.rows = rows;
+    c.out = p;
+    c.lse = lse;
+    int rc = check_shape(&c.sh);
+    if (rc) return rc;
+    rc = check_rows(&c.sh, rows, nrows);
+    if (rc) return rc;
+    return run_rows(softmax_row, &c, nrows, S, nthreads);
+}
+
+/* Step 5 for one row: out[b,h,i,d] = sum_j p[b,h,i,j] v[b,g,j,d]. */
+static void pv_row(void* vctx, int64_t n, double* unused) {
+    (void)unused;
+    const step_ctx* c = (const step_ctx*)vctx;
+    const shape_t* sh = &c->sh;
+    int64_t b, h, i;
+    split_row(sh, c->rows[n], &b, &h, &i);
+    const int64_t g = kv_head(sh, h);
+    const int64_t S = sh->S, D = sh->D;
+    const float* pi = c->a + ((b * sh->Hq + h) * S + i) * S;
+    const float* vb = c->b + (b * sh->Hkv + g) * S * D;
+    double* o = c->out + n * D;
+    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+    for (int64_t j = 0; j < S; ++j) {
+        const double w = (double)pi[j];
+        for (int64_t d = 0; d < D; ++d) o[d] += w * (double)vb[j * D + d];
+    }
+}
+
+/* P V for the listed rows; p is [B,Hq,S,S], v is [B,Hkv,S,D]; out [nrows, D]. */
+int oracle_pv_rows(const float* p, const float* v,
+                   int64_t B, int64_t Hq, int64_t Hkv, int64_t S, int64_t D,
+                   const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+    step_ctx c;
+    memset(&c, 0, sizeof c);
+    c.a = p; c.b = v;
+    c.sh.B = B; c.sh.Hq = Hq; c.sh.Hkv = Hkv; c.sh.S = S; c.sh.D = D;
+    c.rows = rows;
+    c.out = out;
+    int rc = check_shape(&c.sh);
+    if (rc) return rc;
+    rc = check_rows(&c.sh, rows, nrows);
+    if (rc) return rc;
+    return run_rows(pv_row, &c, nrows, 0, nthreads);
+}
+
+/* Which mistake (0 = none) this build carries; lets a test confirm a variant. */
+int oracle_plant_id(void) { return ORACLE_PLANT; }

@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs for the attention forward and the unfused trio.
+
+This module is the only code shared by the HIP path's tests/bench and the CPU
+oracle.  It draws random numbers and rounds them to the storage dtype; it does
+none of the attention arithmetic.
+
+Workload shape follows the tutorial pages: q, k, v are ``[B, H, S, D]`` tensors
+filled with iid standard normals (``torch.randn`` in the Russian tutorial
+"Profiling Attention in PyTorch", section 1).  Here they come from numpy's
+PCG64 (``default_rng(seed).standard_normal(dtype=float32)``), drawn in the
+order q, k, v, then rounded to bfloat16 with round-to-nearest-even when the
+config is bf16.  The oracle and the GPU see bit-identical values: the oracle
+gets the float32 image of each bf16 value (exact), the GPU gets the bf16 bits.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round-to-nearest-even); return uint16 bits.
+
+    Inputs are finite by construction (standard normals), so NaN handling is
+    not needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact float32 image of bfloat16 bit patterns."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class Tensor:
+    """A host tensor in its storage dtype plus its exact float32 image.
+
+    ``bits`` is uint16 (bf16 payload) for bf16, float32 for fp32.
+    ``f32`` holds the exact values as float32 (what the oracle consumes).
+    """
+
+    bits: np.ndarray
+    f32: np.ndarray
+    dtype: str  # "bf16" | "f32"
+
+
+def _finish(x32: np.ndarray, dtype: str) -> Tensor:
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(x32)
+        return Tensor(bits=bits, f32=bf16_bits_to_f32(bits), dtype=dtype)
+    if dtype == "f32":
+        x32 = np.ascontiguousarray(x32, dtype=np.float32)
+        return Tensor(bits=x32, f32=x32, dtype=dtype)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_qkv(B: int, Hq: int, Hkv: int, S: int, D: int, dtype: str, seed: int):
+    """Draw q ``[B,Hq,S,D]``, k and v ``[B,Hkv,S,D]`` iid N(0,1) in that order."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, S, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    return _finish(q, dtype), _finish(k, dtype), _finish(v, dtype)
+
+
+def make_scores(B: int, H: int, S: int, D: int, seed: int) -> np.ndarray:
+    """Raw (unscaled) score-like matrix ``[B,H,S,S]`` fp32 for the masked softmax alone.
+
+    A dot product of two D-long N(0,1) vectors has variance D, so the entries
+    are N(0, D): after the 1/sqrt(D) scale the logits are N(0,1), as they are
+    in the full pipeline.
+    """
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, H, S, S), dtype=np.float32)
+    x *= np.float32(np.sqrt(D))
+    return x
+
+
+def make_probs(B: int, H: int, S: int, causal: bool, dtype: str, seed: int) -> Tensor:
+    """Probability-like matrix ``[B,H,S,S]`` for the PV product alone.
+
+    Row i holds uniform draws in [0, 2/n_i) on its n_i visible keys
+    (n_i = i+1 when causal, S otherwise) and zeros elsewhere, so rows sum to
+    about one and carry the causal zero pattern, like real softmax output.
+    """
+    rng = np.random.default_rng(seed)
+    x = rng.random((B, H, S, S), dtype=np.float32)
+    n = (np.arange(S, dtype=np.float32) + 1.0) if causal else np.full(S, float(S), np.float32)
+    x *= (np.float32(2.0) / n)[:, None]
+    if causal:
+        x *= np.tril(np.ones((S, S), dtype=np.float32))
+    return _finish(x, dtype)
+
+
+# The five workloads of the method's headline measurements.  Seeds are fixed so
+# every run (tests, bench, smoke) sees the same values.
+CONFIGS = {
+    "C1": dict(dtype="f32", B=1, Hq=1, Hkv=1, S=128, D=64, causal=True, seed=1),
+    "C2": dict(dtype="bf16", B=1, Hq=32, Hkv=32, S=2048, D=128, causal=True, seed=2),
+    "C3": dict(dtype="bf16", B=4, Hq=16, Hkv=16, S=4096, D=128, causal=True, seed=3),
+    "C4": dict(dtype="bf16", B=2, Hq=32, Hkv=32, S=8192, D=128, causal=True, seed=4),
+    "C5": dict(dtype="bf16", B=8, Hq=32, Hkv=8, S=4096, D=128, causal=True, seed=5),
+}
+

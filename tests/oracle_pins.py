@@ -1,0 +1,396 @@
+"""Pins for the CPU oracle: facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with the fact it checks.  ``tests/test_oracle_pins.py`` runs
+them on the real oracle (all must pass) and on builds that carry a planted
+mistake (each must be caught by at least one pin).
+
+What pins what:
+  attention forward (formula of the ainews.cool deep-dive; five-step causal
+  pipeline of the Hugging Face article's "Naive Attention" section):
+    hand-derived worked examples (tests/golden/hand_cases.json), the S=2, D=1
+    closed form, causal row 0 = v_0, q = 0 -> running prefix mean of v with
+    lse = ln(i+1), identical keys -> uniform weights, key shift invariance,
+    affinity in v, one-hot v exposing the weights (rows sum to 1, zero above
+    the diagonal, log-ratio = scaled key difference), last causal row = last
+    non-causal row, S = 1, grouped-query heads = repeated heads, the
+    hard-attention limit, and torch's float64 CPU scaled_dot_product_attention
+    plus torch.logsumexp as an independent library routine.
+  step 1 (q k^T): numpy matmul, exact integer products.
+  steps 2-4 (scale, -inf mask, softmax): hand fixtures, scipy.special.softmax
+    and logsumexp, rows sum to one, zero above the diagonal.
+  step 5 (attn v): numpy matmul, exact integer products.
+  composition: steps 1-5 chained equal the fused forward.
+"""
+from __future__ import annotations
+
+import json
+import math
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+
+GOLDEN = Path(__file__).resolve().parent / "golden" / "hand_cases.json"
+
+TIGHT = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, tol=TIGHT, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+def _frac(s) -> float:
+    return float(Fraction(str(s)))
+
+
+def _scale(s) -> float:
+    return {"ln2": math.log(2.0), "ln3": math.log(3.0)}[s] if isinstance(s, str) else float(s)
+
+
+def _randn(shape, seed):
+    return _rng(seed).standard_normal(shape).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# attention forward
+# --------------------------------------------------------------------------
+
+def pin_golden_attention(orc):
+    cases = json.loads(GOLDEN.read_text())
+    tol = cases["tol"]
+    for c in cases["attention"]:
+        q = np.array(c["q"], np.float32)
+        k = np.array(c["k"], np.float32)
+        v = np.array(c["v"], np.float32)
+        out, lse = orc.attn_fwd(q, k, v, _scale(c["scale"]), c["causal"])
+        exp_out = np.vectorize(_frac)(np.array(c["out"], dtype=object)).astype(np.float64)
+        exp_lse = np.log(np.vectorize(_frac)(np.array(c["lse_exp"], dtype=object)).astype(np.float64))
+        _close(out, exp_out, tol, c["name"] + " out")
+        _close(lse, exp_lse, tol, c["name"] + " lse")
+
+
+def pin_s2_d1_closed_form(orc):
+    """S=2, D=1: row 1 = (e^{a} x + e^{b} y) / (e^{a} + e^{b}), a = sc*q1*k0, b = sc*q1*k1."""
+    r = _rng(11)
+    for trial in range(20):
+        qv, kv, vv = (r.standard_normal(2).astype(np.float32) for _ in range(3))
+        sc = float(r.uniform(0.2, 2.0))
+        q = qv.reshape(1, 1, 2, 1)
+        k = kv.reshape(1, 1, 2, 1)
+        v = vv.reshape(1, 1, 2, 1)
+        q64, k64, v64 = qv.astype(np.float64), kv.astype(np.float64), vv.astype(np.float64)
+        for causal in (True, False):
+            out, lse = orc.attn_fwd(q, k, v, sc, causal)
+            a, b = sc * q64[1] * k64[0], sc * q64[1] * k64[1]
+            row1 = (math.exp(a) * v64[0] + math.exp(b) * v64[1]) / (math.exp(a) + math.exp(b))
+            _close(out[0, 0, 1, 0], row1, 1e-12, "S2 row1")
+            _close(lse[0, 0, 1], math.log(math.exp(a) + math.exp(b)), 1e-12, "S2 lse1")
+            if causal:
+                _close(out[0, 0, 0, 0], v64[0], 0.0, "S2 causal row0")
+                _close(lse[0, 0, 0], sc * q64[0] * k64[0], 1e-12, "S2 causal lse0")
+            else:
+                c0, c1 = sc * q64[0] * k64[0], sc * q64[0] * k64[1]
+                row0 = (math.exp(c0) * v64[0] + math.exp(c1) * v64[1]) / (math.exp(c0) + math.exp(c1))
+                _close(out[0, 0, 0, 0], row0, 1e-12, "S2 noncausal row0")
+
+
+def pin_causal_row0(orc):
+    """Causal row 0 sees key 0 only: out = v_0 exactly, lse = scale * q_0 . k_0."""
+    for (B, Hq, Hkv, S, D, seed) in [(2, 4, 2, 37, 16, 1), (1, 3, 1, 5, 64, 2)]:
+        q = _randn((B, Hq, S, D), seed)
+        k = _randn((B, Hkv, S, D), seed + 100)
+        v = _randn((B, Hkv, S, D), seed + 200)
+        sc = 1.0 / math.sqrt(D)
+        out, lse = orc.attn_fwd(q, k, v, sc, True)
+        g = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                kvh = h // g
+                _close(out[b, h, 0], v[b, kvh, 0].astype(np.float64), 0.0, "row0 out")
+                dot = sum(float(q[b, h, 0, d]) * float(k[b, kvh, 0, d]) for d in range(D))
+                _close(lse[b, h, 0], sc * dot, 1e-12, "row0 lse")
+
+
+def pin_zero_queries(orc):
+    """q = 0: all logits 0 -> out_i = mean(v_0..v_i), lse_i = ln(i+1) (causal);
+    mean of all v and ln S otherwise."""
+    B, Hq, Hkv, S, D = 1, 2, 2, 23, 8
+    q = np.zeros((B, Hq, S, D), np.float32)
+    k = _randn((B, Hkv, S, D), 3)
+    v = _randn((B, Hkv, S, D), 4)
+    v64 = v.astype(np.float64)
+    out, lse = orc.attn_fwd(q, k, v, 0.3, True)
+    for i in range(S):
+        _close(out[:, :, i], v64[:, :, : i + 1].mean(axis=2), 1e-12, "zero-q prefix mean")
+        _close(lse[:, :, i], np.full((B, Hq), math.log(i + 1)), 1e-12, "zero-q lse")
+    out, lse = orc.attn_fwd(q, k, v, 0.3, False)
+    for i in range(S):
+        _close(out[:, :, i], v64.mean(axis=2), 1e-12, "zero-q mean")
+        _close(lse[:, :, i], np.full((B, Hq), math.log(S)), 1e-12, "zero-q lse S")
+
+
+def pin_identical_keys(orc):
+    """k_j = kappa for all j: uniform weights; lse_i = scale q_i.kappa + ln(i+1)."""
+    B, H, S, D = 1, 1, 17, 8
+    q = _randn((B, H, S, D), 5)
+    kappa = _randn((D,), 6)
+    k = np.broadcast_to(kappa, (B, H, S, D)).copy()
+    v = _randn((B, H, S, D), 7)
+    sc = 0.7
+    out, lse = orc.attn_fwd(q, k, v, sc, True)
+    v64 = v.astype(np.float64)
+    for i in range(S):
+        _close(out[0, 0, i], v64[0, 0, : i + 1].mean(axis=0), 1e-12, "identical keys out")
+        qk = sum(float(q[0, 0, i, d]) * float(kappa[d]) for d in range(D))
+        _close(lse[0, 0, i], sc * qk + math.log(i + 1), 1e-12, "identical keys lse")
+
+
+def pin_shift_keys(orc):
+    """k_j -> k_j + c: out unchanged, lse_i -> lse_i + scale q_i.c."""
+    B, H, S, D = 1, 2, 19, 4
+    # small integers and halves keep k + c exact in float32
+    r = _rng(8)
+    q = r.integers(-3, 4, (B, H, S, D)).astype(np.float32) / 2
+    k = r.integers(-3, 4, (B, H, S, D)).astype(np.float32) / 2
+    v = _randn((B, H, S, D), 9)
+    c = np.array([0.5, -1.0, 1.5, 2.0], np.float32)
+    sc = 0.4
+    for causal in (True, False):
+        o1, l1 = orc.attn_fwd(q, k, v, sc, causal)
+        o2, l2 = orc.attn_fwd(q, k + c, v, sc, causal)
+        _close(o2, o1, 1e-12, "shift out")
+        _close(l2 - l1, sc * (q.astype(np.float64) @ c.astype(np.float64)), 1e-12, "shift lse")
+
+
+def pin_affine_v(orc):
+    """v -> alpha v + beta: out -> alpha out + beta (weights sum to one)."""
+    B, Hq, Hkv, S, D = 2, 2, 1, 21, 8
+    q = _randn((B, Hq, S, D), 10)
+    k = _randn((B, Hkv, S, D), 11)
+    v = (_rng(12).integers(-8, 9, (B, Hkv, S, D))).astype(np.float32)
+    alpha, beta = 0.5, 3.0
+    for causal in (True, False):
+        o1, _ = orc.attn_fwd(q, k, v, 0.35, causal)
+        o2, _ = orc.attn_fwd(q, k, (alpha * v + beta).astype(np.float32), 0.35, causal)
+        _close(o2, alpha * o1 + beta, 1e-11, "affine v")
+
+
+def pin_onehot_weights(orc):
+    """v = identity (D = S) makes out the weight matrix itself."""
+    S = 12
+    q = _randn((1, 1, S, 6), 13)
+    k = _randn((1, 1, S, 6), 14)
+    sc = 0.6
+    q6 = np.zeros((1, 1, S, S), np.float32)
+    k6 = np.zeros((1, 1, S, S), np.float32)
+    q6[..., :6] = q
+    k6[..., :6] = k
+    v = np.eye(S, dtype=np.float32).reshape(1, 1, S, S)
+    for causal in (True, False):
+        w, _ = orc.attn_fwd(q6, k6, v, sc, causal)
+        w = w[0, 0]
+        assert np.all(w >= 0), "weights negative"
+        _close(w.sum(axis=1), np.ones(S), 1e-12, "weights sum")
+        if causal:
+            assert np.all(np.triu(w, 1) == 0.0), "weight above the diagonal"
+        q64, k64 = q[0, 0].astype(np.float64), k[0, 0].astype(np.float64)
+        for i in range(S):
+            jmax = i if causal else S - 1
+            for j in range(jmax + 1):
+                expect = sc * float(q64[i] @ (k64[j] - k64[0]))
+                _close(math.log(w[i, j]) - math.log(w[i, 0]), expect, 1e-10, "log-ratio")
+
+
+def pin_last_row(orc):
+    """The last causal row sees every key, as the non-causal row does."""
+    q = _randn((2, 2, 33, 16), 15)
+    k = _randn((2, 2, 33, 16), 16)
+    v = _randn((2, 2, 33, 16), 17)
+    oc, lc = orc.attn_fwd(q, k, v, 0.25, True)
+    on, ln_ = orc.attn_fwd(q, k, v, 0.25, False)
+    _close(oc[:, :, -1], on[:, :, -1], 1e-13, "last row out")
+    _close(lc[:, :, -1], ln_[:, :, -1], 1e-13, "last row lse")
+
+
+def pin_s1(orc):
+    """S = 1: out = v, lse = scale q.k (both modes)."""
+    q = _randn((3, 4, 1, 64), 18)
+    k = _randn((3, 2, 1, 64), 19)
+    v = _randn((3, 2, 1, 64), 20)
+    for causal in (True, False):
+        out, lse = orc.attn_fwd(q, k, v, 0.125, causal)
+        kk = np.repeat(k, 2, axis=1).astype(np.float64)
+        vv = np.repeat(v, 2, axis=1).astype(np.float64)
+        _close(out, vv, 0.0, "S1 out")
+        _close(lse, 0.125 * np.sum(q.astype(np.float64) * kk, axis=-1), 1e-12, "S1 lse")
+
+
+def pin_gqa(orc):
+    """Hkv < Hq equals multi-head attention with k, v repeated per group
+    (query head h reads key/value head h // (Hq/Hkv))."""
+    B, Hq, Hkv, S, D = 2, 6, 2, 14, 8
+    q = _randn((B, Hq, S, D), 21)
+    k = _randn((B, Hkv, S, D), 22)
+    v = _randn((B, Hkv, S, D), 23)
+    for causal in (True, False):
+        o1, l1 = orc.attn_fwd(q, k, v, 0.3, causal)
+        o2, l2 = orc.attn_fwd(q, np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1), 0.3, causal)
+        _close(o1, o2, 0.0, "gqa out")
+        _close(l1, l2, 0.0, "gqa lse")
+
+
+def pin_hard_limit(orc):
+    """Large scale: the weight concentrates on the largest logit, out -> v_argmax."""
+    B, H, S, D = 1, 1, 16, 4
+    r = _rng(24)
+    q = r.integers(-4, 5, (B, H, S, D)).astype(np.float32)
+    k = r.integers(-4, 5, (B, H, S, D)).astype(np.float32)
+    v = _randn((B, H, S, D), 25)
+    sc = 60.0
+    for causal in (True, False):
+        out, _ = orc.attn_fwd(q, k, v, sc, causal)
+        for i in range(S):
+            jmax = i if causal else S - 1
+            dots = [int(np.dot(q[0, 0, i].astype(np.int64), k[0, 0, j].astype(np.int64))) for j in range(jmax + 1)]
+            best = max(dots)
+            if dots.count(best) != 1:
+                continue  # tie: the limit averages the tied values
+            j = dots.index(best)
+            _close(out[0, 0, i], v[0, 0, j].astype(np.float64), 1e-6, "hard limit")
+
+
+def pin_torch_sdpa(orc):
+    """torch's float64 CPU scaled_dot_product_attention (an independent library
+    implementation) and torch.logsumexp agree with the oracle."""
+    import torch
+
+    for (B, Hq, Hkv, S, D, seed) in [(2, 4, 4, 29, 16, 30), (1, 6, 2, 40, 32, 31), (1, 2, 1, 7, 64, 32)]:
+        q = _randn((B, Hq, S, D), seed)
+        k = _randn((B, Hkv, S, D), seed + 1)
+        v = _randn((B, Hkv, S, D), seed + 2)
+        sc = 1.0 / math.sqrt(D)
+        g = Hq // Hkv
+        tq = torch.from_numpy(q.astype(np.float64))
+        tk = torch.from_numpy(k.astype(np.float64)).repeat_interleave(g, dim=1)
+        tv = torch.from_numpy(v.astype(np.float64)).repeat_interleave(g, dim=1)
+        for causal in (True, False):
+            ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=sc)
+            logits = torch.matmul(tq, tk.transpose(-2, -1)) * sc
+            if causal:
+                mask = torch.ones(S, S, dtype=torch.bool).triu(1)
+                logits = logits.masked_fill(mask, float("-inf"))
+            ref_lse = torch.logsumexp(logits, dim=-1)
+            out, lse = orc.attn_fwd(q, k, v, sc, causal)
+            _close(out, ref.numpy(), 1e-12, "torch sdpa out")
+            _close(lse, ref_lse.numpy(), 1e-12, "torch lse")
+
+
+ATTN_PINS = [
+    pin_golden_attention, pin_s2_d1_closed_form, pin_causal_row0, pin_zero_queries,
+    pin_identical_keys, pin_shift_keys, pin_affine_v, pin_onehot_weights, pin_last_row,
+    pin_s1, pin_gqa, pin_hard_limit, pin_torch_sdpa,
+]
+
+
+# --------------------------------------------------------------------------
+# unfused steps
+# --------------------------------------------------------------------------
+
+def pin_qk_numpy(orc):
+    """Step 1 equals numpy's matmul (per kv-head group)."""
+    B, Hq, Hkv, S, D = 2, 4, 2, 19, 24
+    q = _randn((B, Hq, S, D), 40)
+    k = _randn((B, Hkv, S, D), 41)
+    ref = np.matmul(q.astype(np.float64), np.repeat(k, 2, axis=1).astype(np.float64).transpose(0, 1, 3, 2))
+    _close(orc.qk_scores(q, k), ref, 1e-12, "qk numpy")
+    rows = np.array([0, 5, B * Hq * S - 1], np.int64)
+    _close(orc.qk_scores(q, k, rows=rows), ref.reshape(-1, S)[rows], 1e-12, "qk rows")
+
+
+def pin_qk_integer(orc):
+    """Step 1 on small integers is exact: compare with int64 arithmetic."""
+    r = _rng(42)
+    q = r.integers(-9, 10, (1, 2, 9, 7))
+    k = r.integers(-9, 10, (1, 2, 9, 7))
+    ref = np.matmul(q, k.transpose(0, 1, 3, 2)).astype(np.float64)
+    _close(orc.qk_scores(q.astype(np.float32), k.astype(np.float32)), ref, 0.0, "qk exact")
+
+
+def pin_golden_softmax(orc):
+    cases = json.loads(GOLDEN.read_text())
+    for c in cases["masked_softmax"]:
+        x = np.array(c["x"], np.float32)
+        p, lse = orc.masked_softmax(x, _scale(c["scale"]), c["causal"])
+        exp_p = np.vectorize(_frac)(np.array(c["p"], dtype=object)).astype(np.float64)
+        exp_lse = np.log(np.vectorize(_frac)(np.array(c["lse_exp"], dtype=object)).astype(np.float64))
+        _close(p, exp_p, cases["tol"], c["name"] + " p")
+        _close(lse, exp_lse, cases["tol"], c["name"] + " lse")
+
+
+def pin_softmax_scipy(orc):
+    """Steps 2-4 equal scipy.special.softmax / logsumexp on the masked,
+    scaled logits; rows sum to one; entries above the diagonal are zero."""
+    from scipy.special import logsumexp, softmax
+
+    B, H, S = 2, 3, 31
+    x = _randn((B, H, S, S), 43) * 8
+    sc = 0.2
+    for causal in (True, False):
+        t = sc * x.astype(np.float64)
+        if causal:
+            t = np.where(np.triu(np.ones((S, S), bool), 1), -np.inf, t)
+        p, lse = orc.masked_softmax(x, sc, causal)
+        _close(p, softmax(t, axis=-1), 1e-13, "softmax scipy")
+        _close(lse, logsumexp(t, axis=-1), 1e-12, "lse scipy")
+        _close(p.sum(axis=-1), np.ones((B, H, S)), 1e-12, "rows sum")
+        if causal:
+            assert np.all(p[..., np.triu(np.ones((S, S), bool), 1)] == 0.0)
+
+
+def pin_pv_numpy(orc):
+    """Step 5 equals numpy's matmul (per kv-head group)."""
+    B, Hq, Hkv, S, D = 2, 4, 1, 17, 12
+    p = _rng(44).random((B, Hq, S, S)).astype(np.float32)
+    v = _randn((B, Hkv, S, D), 45)
+    ref = np.matmul(p.astype(np.float64), np.repeat(v, 4, axis=1).astype(np.float64))
+    _close(orc.pv(p, v), ref, 1e-12, "pv numpy")
+
+
+def pin_pv_integer(orc):
+    r = _rng(46)
+    p = r.integers(-5, 6, (1, 1, 11, 11))
+    v = r.integers(-5, 6, (1, 1, 11, 3))
+    _close(orc.pv(p.astype(np.float32), v.astype(np.float32)), np.matmul(p, v).astype(np.float64), 0.0, "pv exact")
+
+
+def pin_chain_equals_fused(orc):
+    """Steps 1-5 chained give the fused forward's out and lse."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 26, 16
+    q = _randn((B, Hq, S, D), 47)
+    k = _randn((B, Hkv, S, D), 48)
+    v = _randn((B, Hkv, S, D), 49)
+    sc = 0.25
+    for causal in (True, False):
+        scores = orc.qk_scores(q, k)
+        # the chain's hand-offs are float32 here only because the oracle's
+        # inputs are float32 arrays; compare at float32 resolution
+        p, lse = orc.masked_softmax(scores.astype(np.float32), sc, causal)
+        out = orc.pv(p.astype(np.float32), v)
+        fo, fl = orc.attn_fwd(q, k, v, sc, causal)
+        _close(out, fo, 1e-5, "chain out")
+        _close(lse, fl, 1e-5, "chain lse")
+
+
+STEP_PINS = [pin_qk_numpy, pin_qk_integer, pin_golden_softmax, pin_softmax_scipy,
+             pin_pv_numpy, pin_pv_integer, pin_chain_equals_fused]
+
+ALL_PINS = ATTN_PINS + STEP_PINS
