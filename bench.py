@@ -1,0 +1,297 @@
+"""Benchmark of libattn's fused causal attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload: causal attention forward, bf16, B=4 H=16 S=4096 D=128 (the shape of
+the tutorials' comparison table), q/k/v iid N(0,1) from a fixed seed,
+resident in HBM before timing starts.  One step = one attn_fwd_bf16 launch.
+
+Prints ONE JSON line with the throughput (TFLOP/s, causal FLOPs counted as
+2*B*H*S^2*D), the roofline of the fused kernel (achieved vs dense bf16 MFMA
+peak, measured with HIP events on the launch stream), the unfused trio at the
+same shape (u2 judged on HBM GB/s), and the CPU oracle timed on a bounded
+sample of the same workload on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "fused causal attn fwd TFLOP/s + % bf16 MFMA peak (B4 H16 S4096 D128)"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILE = ROOT / "profiles" / "fwd_bf16_B4H16S4096D128_causal.md"
+KERNEL_SOURCES = ["fwd_bf16.hip", "kv_tile.h", "common.h"]
+
+
+def attn_flops(B, H, S, D, causal):
+    f = 2.0 * B * H * S * S * D
+    return f if causal else 2.0 * f
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES:
+        h.update((ROOT / "scaled_dot_product_10_amd" / "csrc" / n).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the summary is missing or was taken on other kernel source."""
+    if not PROFILE.exists():
+        return None
+    text = PROFILE.read_text()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_hash and m_bytes) or m_hash.group(1) != kernel_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def host_threads() -> int:
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_launches(fn, iters, stream):
+    """Per-launch HIP-event durations (ms) on the launch stream."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for s, e in ev:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
+
+
+def cpu_baseline(q, k, v, B, Hq, S, D, sc, seconds=12.0, seed=123):
+    """The fp64 CPU oracle on random rows of the same workload until ~seconds
+    of wall time; rate in TFLOP/s with the same causal FLOP convention."""
+    import oracle
+
+    orc = oracle.default()
+    threads = host_threads()
+    rng = np.random.default_rng(seed)
+    done_rows, flops, t_total = 0, 0.0, 0.0
+    chunk = 2048
+    while t_total < seconds:
+        rows = rng.integers(0, B * Hq * S, chunk)
+        i = rows % S
+        t0 = time.perf_counter()
+        orc.attn_fwd(q.f32, k.f32, v.f32, sc, True, rows=rows, nthreads=threads)
+        t_total += time.perf_counter() - t0
+        flops += float(np.sum(4.0 * (i + 1) * D))  # q.k and p.v over the i+1 visible keys
+        done_rows += chunk
+        if t_total < 1.0:
+            chunk *= 2
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done_rows} random query rows of the B4 H16 S4096 D128 causal workload "
+                  f"({flops / 1e9:.1f} GFLOP, {t_total:.1f} s, fp64, {cpu_model()})",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference kernel for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); libattn is a single-GPU build",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from scaled_dot_product_10_amd import _lib, api, inputs
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    _lib.lib()
+    dev = torch.device("cuda:0")
+    c = inputs.CONFIGS["C3"]
+    B, Hq, Hkv, S, D = c["B"], c["Hq"], c["Hkv"], c["S"], c["D"]
+    sc = 1.0 / math.sqrt(D)
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", c["seed"])
+
+    def to_dev(t):
+        return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    out = torch.empty_like(dq)
+    lse = torch.empty((B, Hq, S), device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def fused(causal=True):
+        rc = _lib.attn_fwd_bf16(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                B, Hq, Hkv, S, D, sc, int(causal), sp)
+        if rc:
+            raise _lib.AttnError(rc, "attn_fwd_bf16")
+
+    if args.calib_copy:
+        # a plain copy of known size: 1 GiB read + 1 GiB written
+        src = torch.ones(1 << 28, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize()
+    # timed region: exactly K steps, synchronised on both sides
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        fused()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    flops = attn_flops(B, Hq, S, D, True)
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    # per-launch durations for the roofline (same stream)
+    per = time_launches(fused, max(args.steps, 10), stream)
+    ms_launch = float(np.mean(per))
+    achieved = flops / (ms_launch * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": profiled_traffic(),
+        "kernel": "fwd_bf16_kernel<128, causal>",
+        "launch_ms_mean": round(ms_launch, 4),
+        "launch_ms_min": round(float(np.min(per)), 4),
+        "algorithmic_bytes": int(2 * B * Hq * S * D * 2 + 2 * B * Hkv * S * D * 2 + B * Hq * S * 4),
+    }
+
+    # non-causal fused, context
+    per_nc = time_launches(lambda: fused(False), 10, stream)
+    nc_ms = float(np.median(per_nc))
+    noncausal = {"ms": round(nc_ms, 4),
+                 "tflops": round(attn_flops(B, Hq, S, D, False) / (nc_ms * 1e-3) / 1e12, 2)}
+
+    unfused = None
+    if not args.no_unfused:
+        scores = torch.empty((B, Hq, S, S), device=dev, dtype=torch.float32)
+        p = torch.empty((B, Hq, S, S), device=dev, dtype=torch.bfloat16)
+        uo = torch.empty_like(dq)
+        ul = torch.empty((B, Hq, S), device=dev, dtype=torch.float32)
+
+        def u1():
+            assert _lib.attn_qk_gemm_bf16(dq.data_ptr(), dk.data_ptr(), scores.data_ptr(), B, Hq, Hkv, S, D, sp) == 0
+
+        def u2():
+            assert _lib.attn_masked_softmax_bf16(scores.data_ptr(), p.data_ptr(), ul.data_ptr(), B, Hq, S, sc, 1,
+                                                 sp) == 0
+
+        def u3():
+            assert _lib.attn_pv_gemm_bf16(p.data_ptr(), dv.data_ptr(), uo.data_ptr(), B, Hq, Hkv, S, D, sp) == 0
+
+        for f in (u1, u2, u3):
+            f()
+        torch.cuda.synchronize()
+        t_u = {}
+        for name, f in (("qk_gemm", u1), ("masked_softmax", u2), ("pv_gemm", u3)):
+            t_u[name] = float(np.median(time_launches(f, 5, stream)))
+        n_el = B * Hq * S * S
+        # algorithmic bytes: u1 writes fp32 scores; u2 reads the unmasked (causal) part, writes bf16 p;
+        # u3 reads bf16 p and v, writes out
+        b_u1 = n_el * 4 + (B * Hq + B * Hkv) * S * D * 2
+        b_u2 = B * Hq * (S * (S + 1) // 2) * 4 + n_el * 2 + B * Hq * S * 4
+        b_u3 = n_el * 2 + B * Hkv * S * D * 2 + B * Hq * S * D * 2
+        gbs = lambda b, ms: round(b / (ms * 1e-3) / 1e9, 1)
+        total = sum(t_u.values())
+        unfused = {
+            "ms": {k_: round(v_, 4) for k_, v_ in t_u.items()},
+            "total_ms": round(total, 4),
+            "fused_speedup": round(total / ms_step, 2),
+            "qk_gemm": {"GB/s": gbs(b_u1, t_u["qk_gemm"]), "bytes": b_u1},
+            "masked_softmax": {"GB/s": gbs(b_u2, t_u["masked_softmax"]), "bytes": b_u2,
+                               "roofline": {"bound": "hbm", "achieved": gbs(b_u2, t_u["masked_softmax"]),
+                                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                            "frac": round(gbs(b_u2, t_u["masked_softmax"]) / PEAK_HBM_GBS, 4)}},
+            "pv_gemm": {"GB/s": gbs(b_u3, t_u["pv_gemm"]), "bytes": b_u3},
+        }
+        del scores, p
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(q, k, v, B, Hq, S, D, sc, seconds=args.cpu_seconds)
+
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: q,k,v iid N(0,1) (numpy PCG64 seed 3) rounded to bf16",
+        "config": {"workload": "causal attention forward B4 H16 S4096 D128 bf16 (fused, one launch per step)",
+                   "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "D": D, "causal": True, "scale": sc,
+                   "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "noncausal": noncausal,
+        "unfused": unfused,
+        "gpu": props.name,
+        "cus": props.multi_processor_count,
+        "timed_wall_s": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,142 @@
+/*
+ * attn.h -- libattn: causal scaled dot-product attention forward for AMD
+ * MI355X (gfx950), as a plain C ABI.
+ *
+ * The operation is the one the four attention-profiling pages describe:
+ *
+ *     out = softmax(scale * q k^T + mask) v
+ *
+ * (the formula in the ainews.cool article's technical deep-dive; the five-step
+ * causal pipeline -- q k^T, times scale, masked_fill with -inf where key j is
+ * after query i, softmax over keys, times v -- in the "Naive Attention"
+ * section of the Hugging Face "Profiling in PyTorch (Part 3)" article).
+ *
+ * Two ways to compute it are exported:
+ *   - attn_fwd_*: one fused kernel.  Keys and values stream through on-chip
+ *     memory in tiles and the softmax is computed online, so the S x S score
+ *     matrix never reaches device memory (the tiling idea of the Flash
+ *     backend section of the Hugging Face article).
+ *   - the unfused trio attn_qk_gemm_* -> attn_masked_softmax_* ->
+ *     attn_pv_gemm_*, three kernels that materialise scores and
+ *     probabilities in caller-owned buffers, mirroring the naive pipeline.
+ *
+ * Conventions shared by every call
+ *   Layout     q and out are [B, Hq, S, D]; k and v are [B, Hkv, S, D];
+ *              scores and probabilities are [B, Hq, S, S]; lse is [B, Hq, S].
+ *              All row-major and contiguous, D (or the key axis) fastest:
+ *              the native [B, H, S, D] layout the cuDNN section of the
+ *              Hugging Face article praises, with no transposes.
+ *   Heads      Grouped-query attention: query head h reads key/value head
+ *              h / (Hq / Hkv).  Hq must be a multiple of Hkv; Hkv = 1 is
+ *              multi-query attention, Hkv = Hq ordinary multi-head.
+ *   Mask       causal = 1 masks key j for query i when j > i (one shared
+ *              sequence length S, so top-left and bottom-right alignment
+ *              coincide); causal = 0 masks nothing.  Masked logits are -inf
+ *              and get weight exactly 0.
+ *   lse        Natural log of sum_j exp(scale * q_i . k_j) over unmasked j,
+ *              float32.  Not on the pages; kept for a later backward pass or
+ *              a merge of partial results.
+ *   dtype      The _bf16 calls take and return bfloat16 tensors (passed as
+ *              void*) and accumulate in float32; the probabilities handed to
+ *              the second product are rounded to bfloat16 (round to nearest
+ *              even).  The _f32 calls are float32 throughout.
+ *   Sizes      B, Hq, Hkv, S >= 1; D must be 64 or 128.
+ *   Memory     Every pointer is device memory owned by the caller.  The
+ *              library allocates nothing, keeps no state between calls and is
+ *              safe to call from several host threads.  q, k, v, out, scores
+ *              and p must be 16-byte aligned; lse 4-byte aligned.  Outputs
+ *              must not overlap inputs.
+ *   Streams    stream is a hipStream_t passed as void*; NULL means the null
+ *              stream.  Calls are asynchronous: they enqueue kernels and
+ *              return.  A kernel fault shows up at the caller's next
+ *              synchronisation, as usual for HIP.
+ *   Errors     Arguments are checked before anything is enqueued; a failed
+ *              check returns its code, launches nothing and leaves every
+ *              output untouched.  ATTN_ERR_HIP means the launch itself
+ *              failed; attn_last_hip_error() gives the HIP error code
+ *              (per host thread).
+ */
+#ifndef LIBATTN_ATTN_H
+#define LIBATTN_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL_POINTER = 1, /* a required pointer is NULL                          */
+    ATTN_ERR_BAD_SHAPE = 2,    /* a size < 1, Hq % Hkv != 0, or a size overflows      */
+    ATTN_ERR_UNSUPPORTED = 3,  /* D not in {64, 128}, or causal not in {0, 1}         */
+    ATTN_ERR_BAD_SCALE = 4,    /* scale is NaN or infinite                            */
+    ATTN_ERR_MISALIGNED = 5,   /* a tensor pointer breaks the alignment rule          */
+    ATTN_ERR_ALIAS = 6,        /* an output overlaps an input                         */
+    ATTN_ERR_HIP = 7           /* the HIP launch failed; see attn_last_hip_error()    */
+} attn_status;
+
+/* ---------------------------------------------------------------------------
+ * Fused forward (the hot path).
+ *
+ * out[b,h,i,:] = sum_j w_ij v[b,g,j,:],  w_ij = exp(s_ij - lse_i),
+ * s_ij = scale * q[b,h,i,:] . k[b,g,j,:],  g = h / (Hq/Hkv),
+ * over the unmasked j; lse[b,h,i] = ln sum_j exp(s_ij).
+ *
+ * q, k, v, out: bfloat16 (attn_fwd_bf16) or float32 (attn_fwd_f32).
+ * lse: float32 [B,Hq,S], or NULL to skip writing it.
+ * One kernel launch, no workspace.  The usual scale is 1/sqrt(D) (the scale
+ * of the NaiveCausalAttention class in the Hugging Face article).
+ * ------------------------------------------------------------------------- */
+attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Hq, int Hkv, int S, int D, float scale, int causal,
+                          void* stream);
+attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse,
+                         int B, int Hq, int Hkv, int S, int D, float scale, int causal,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Unfused trio, mirroring the naive pipeline one step per kernel.
+ *
+ * Step 1, attn_qk_gemm_*: scores[b,h,i,j] = q[b,h,i,:] . k[b,g,j,:] for every
+ *   i and j (unscaled, unmasked), float32 [B,Hq,S,S] (attn_scores_bytes).
+ * Steps 2-4, attn_masked_softmax_*: p[b,h,i,j] = exp(t_ij - lse_i) with
+ *   t_ij = scale * scores[b,h,i,j], or -inf (so p = 0) for masked j; p is
+ *   [B,H,S,S] in the call's dtype (attn_probs_bytes); lse [B,H,S] float32 or
+ *   NULL.  H is the number of query heads.  The mask is applied on the fly:
+ *   masked entries of scores are never read and need not hold data.
+ * Step 5, attn_pv_gemm_*: out[b,h,i,:] = sum_j p[b,h,i,j] v[b,g,j,:], a plain
+ *   product over every j (zeros in p are multiplied like any value); out is
+ *   [B,Hq,S,D] in the call's dtype.
+ * Each call is one kernel launch on stream.
+ * ------------------------------------------------------------------------- */
+attn_status attn_qk_gemm_bf16(const void* q, const void* k, float* scores,
+                              int B, int Hq, int Hkv, int S, int D, void* stream);
+attn_status attn_qk_gemm_f32(const float* q, const float* k, float* scores,
+                             int B, int Hq, int Hkv, int S, int D, void* stream);
+attn_status attn_masked_softmax_bf16(const float* scores, void* p, float* lse,
+                                     int B, int H, int S, float scale, int causal, void* stream);
+attn_status attn_masked_softmax_f32(const float* scores, float* p, float* lse,
+                                    int B, int H, int S, float scale, int causal, void* stream);
+attn_status attn_pv_gemm_bf16(const void* p, const void* v, void* out,
+                              int B, int Hq, int Hkv, int S, int D, void* stream);
+attn_status attn_pv_gemm_f32(const float* p, const float* v, float* out,
+                             int B, int Hq, int Hkv, int S, int D, void* stream);
+
+/* Bytes of the float32 score buffer: B*Hq*S*S*4, or 0 if a size is < 1 or
+ * the product overflows size_t. */
+size_t attn_scores_bytes(int B, int Hq, int S);
+/* Bytes of the probability buffer: B*Hq*S*S*elem_bytes (2 for bf16, 4 for
+ * float32), or 0 on a bad size. */
+size_t attn_probs_bytes(int B, int Hq, int S, int elem_bytes);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_str(attn_status status);
+/* The hipError_t of this host thread's last ATTN_ERR_HIP, or 0. */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_ATTN_H */

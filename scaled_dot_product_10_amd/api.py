@@ -1,0 +1,142 @@
+"""torch-tensor front end of libattn.
+
+PyTorch only provides device memory and the current stream here: every
+function checks tensor dtypes/devices/contiguity, allocates the outputs with
+torch, and hands raw pointers to the C ABI, which launches libattn's own
+kernels.  A non-zero status raises :class:`AttnError`.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import AttnError
+
+_SUFFIX = {torch.bfloat16: "bf16", torch.float32: "f32"}
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(t: torch.Tensor, name: str, dtype=None, ndim=4):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (libattn has no CPU path)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _raise(code: int, name: str):
+    if code != _lib.ATTN_OK:
+        raise AttnError(code, name)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = True, scale: float | None = None,
+        out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True):
+    """Fused attention forward.  q ``[B,Hq,S,D]``, k/v ``[B,Hkv,S,D]``, bf16 or fp32.
+
+    Returns ``(out, lse)``; ``lse`` is float32 ``[B,Hq,S]`` (None if ``lse=False``).
+    ``scale`` defaults to 1/sqrt(D).
+    """
+    if q.dtype not in _SUFFIX:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, n, q.dtype)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, S, D) or tuple(v.shape) != (B, Hkv, S, D):
+        raise ValueError(f"k/v shapes {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", q.dtype)
+    if lse is True:
+        lse = torch.empty((B, Hq, S), device=q.device, dtype=torch.float32)
+    elif lse is False:
+        lse = None
+    elif lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+    fn = getattr(_lib, "attn_fwd_" + _SUFFIX[q.dtype])
+    code = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+              B, Hq, Hkv, S, D, float(scale), int(bool(causal)), _stream(q.device))
+    _raise(code, "attn_fwd_" + _SUFFIX[q.dtype])
+    return out, lse
+
+
+def qk_gemm(q: torch.Tensor, k: torch.Tensor, scores: torch.Tensor | None = None) -> torch.Tensor:
+    """Step 1: float32 scores ``[B,Hq,S,S]`` = q k^T (unscaled, unmasked)."""
+    if q.dtype not in _SUFFIX:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if scores is None:
+        scores = torch.empty((B, Hq, S, S), device=q.device, dtype=torch.float32)
+    else:
+        _check(scores, "scores", torch.float32)
+    fn = getattr(_lib, "attn_qk_gemm_" + _SUFFIX[q.dtype])
+    _raise(fn(q.data_ptr(), k.data_ptr(), scores.data_ptr(), B, Hq, Hkv, S, D, _stream(q.device)),
+           "attn_qk_gemm_" + _SUFFIX[q.dtype])
+    return scores
+
+
+def masked_softmax(scores: torch.Tensor, *, scale: float, causal: bool = True, dtype=torch.bfloat16,
+                   p: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True):
+    """Steps 2-4: p = softmax(scale * scores + mask) in ``dtype``; returns ``(p, lse)``."""
+    _check(scores, "scores", torch.float32)
+    B, H, S, S2 = scores.shape
+    if S != S2:
+        raise ValueError("scores must be [B,H,S,S]")
+    if dtype not in _SUFFIX:
+        raise TypeError(f"unsupported dtype {dtype}")
+    if p is None:
+        p = torch.empty((B, H, S, S), device=scores.device, dtype=dtype)
+    else:
+        _check(p, "p", dtype)
+    if lse is True:
+        lse = torch.empty((B, H, S), device=scores.device, dtype=torch.float32)
+    elif lse is False:
+        lse = None
+    fn = getattr(_lib, "attn_masked_softmax_" + _SUFFIX[dtype])
+    _raise(fn(scores.data_ptr(), p.data_ptr(), lse.data_ptr() if lse is not None else None, B, H, S, float(scale),
+              int(bool(causal)), _stream(scores.device)), "attn_masked_softmax_" + _SUFFIX[dtype])
+    return p, lse
+
+
+def pv_gemm(p: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Step 5: out ``[B,Hq,S,D]`` = p v in p's dtype."""
+    if p.dtype not in _SUFFIX:
+        raise TypeError(f"unsupported dtype {p.dtype}")
+    _check(p, "p", p.dtype)
+    _check(v, "v", p.dtype)
+    B, Hq, S, _ = p.shape
+    Hkv, D = v.shape[1], v.shape[3]
+    if out is None:
+        out = torch.empty((B, Hq, S, D), device=p.device, dtype=p.dtype)
+    else:
+        _check(out, "out", p.dtype)
+    fn = getattr(_lib, "attn_pv_gemm_" + _SUFFIX[p.dtype])
+    _raise(fn(p.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, S, D, _stream(p.device)),
+           "attn_pv_gemm_" + _SUFFIX[p.dtype])
+    return out
+
+
+def unfused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = True, scale: float | None = None):
+    """The three unfused steps back to back (three launches).  Returns ``(out, lse)``."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    scores = qk_gemm(q, k)
+    p, lse = masked_softmax(scores, scale=scale, causal=causal, dtype=q.dtype)
+    del scores
+    return pv_gemm(p, v), lse

@@ -1,0 +1,264 @@
+// C ABI of libattn (declared in include/attn.h): argument checks, then one
+// kernel launch per call.  Checks run before any HIP call, so a rejected call
+// has no side effect at all.
+#include <math.h>
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxGrid = 0x7fffffff;  // workgroups per launch
+
+bool bad_dims(int B, int Hq, int Hkv, int S) {
+    return B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Hq % Hkv != 0;
+}
+
+bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
+
+// Byte ranges [p, p + n) overlap?
+bool overlap(const void* p, int64_t n, const void* q, int64_t m) {
+    if (!p || !q || n <= 0 || m <= 0) return false;
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + (uintptr_t)m && b < a + (uintptr_t)n;
+}
+
+// Product of sizes, or -1 if it does not fit in int64 with room to spare.
+int64_t prod(std::initializer_list<int64_t> xs) {
+    int64_t r = 1;
+    for (int64_t x : xs) {
+        if (x <= 0) return -1;
+        if (r > (int64_t(1) << 62) / x) return -1;
+        r *= x;
+    }
+    return r;
+}
+
+attn_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return ATTN_OK;
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_HIP;
+}
+
+// Shared checks of the fused forward.  esz = element bytes.
+attn_status check_fwd(const void* q, const void* k, const void* v, const void* out, const float* lse, int B,
+                      int Hq, int Hkv, int S, int D, float scale, int causal, int esz) {
+    if (!q || !k || !v || !out) return ATTN_ERR_NULL_POINTER;
+    if (bad_dims(B, Hq, Hkv, S)) return ATTN_ERR_BAD_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_BAD_SCALE;
+    const int64_t nq = prod({B, Hq, S, D, esz});
+    const int64_t nkv = prod({B, Hkv, S, D, esz});
+    const int64_t nl = prod({B, Hq, S, 4});
+    if (nq < 0 || nkv < 0 || nl < 0) return ATTN_ERR_BAD_SHAPE;
+    if (prod({B, Hq, (S + 63) / 64}) > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
+        misaligned(lse, 4))
+        return ATTN_ERR_MISALIGNED;
+    if (overlap(out, nq, q, nq) || overlap(out, nq, k, nkv) || overlap(out, nq, v, nkv) ||
+        overlap(lse, nl, q, nq) || overlap(lse, nl, k, nkv) || overlap(lse, nl, v, nkv) ||
+        overlap(lse, nl, out, nq))
+        return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+attn_status check_qk(const void* q, const void* k, const float* scores, int B, int Hq, int Hkv, int S, int D,
+                     int esz) {
+    if (!q || !k || !scores) return ATTN_ERR_NULL_POINTER;
+    if (bad_dims(B, Hq, Hkv, S)) return ATTN_ERR_BAD_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    const int64_t nq = prod({B, Hq, S, D, esz});
+    const int64_t nk = prod({B, Hkv, S, D, esz});
+    const int64_t ns = prod({B, Hq, S, S, 4});
+    if (nq < 0 || nk < 0 || ns < 0) return ATTN_ERR_BAD_SHAPE;
+    const int64_t t = (S + 127) / 128, t64 = (S + 63) / 64;
+    if (prod({B, Hq, t, t}) > kMaxGrid || prod({B, Hq, t64, t64}) > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(scores, 16)) return ATTN_ERR_MISALIGNED;
+    if (overlap(scores, ns, q, nq) || overlap(scores, ns, k, nk)) return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+attn_status check_softmax(const float* scores, const void* p, const float* lse, int B, int H, int S, float scale,
+                          int causal, int esz) {
+    if (!scores || !p) return ATTN_ERR_NULL_POINTER;
+    if (B < 1 || H < 1 || S < 1) return ATTN_ERR_BAD_SHAPE;
+    if (causal != 0 && causal != 1) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_BAD_SCALE;
+    const int64_t ns = prod({B, H, S, S, 4});
+    const int64_t np = prod({B, H, S, S, esz});
+    const int64_t nl = prod({B, H, S, 4});
+    if (ns < 0 || np < 0 || nl < 0) return ATTN_ERR_BAD_SHAPE;
+    if (prod({B, H, (S + 3) / 4}) > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+    if (misaligned(scores, 16) || misaligned(p, 16) || misaligned(lse, 4)) return ATTN_ERR_MISALIGNED;
+    if (overlap(p, np, scores, ns) || overlap(lse, nl, scores, ns) || overlap(lse, nl, p, np))
+        return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+attn_status check_pv(const void* p, const void* v, const void* out, int B, int Hq, int Hkv, int S, int D, int esz) {
+    if (!p || !v || !out) return ATTN_ERR_NULL_POINTER;
+    if (bad_dims(B, Hq, Hkv, S)) return ATTN_ERR_BAD_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    const int64_t np = prod({B, Hq, S, S, esz});
+    const int64_t nv = prod({B, Hkv, S, D, esz});
+    const int64_t no = prod({B, Hq, S, D, esz});
+    if (np < 0 || nv < 0 || no < 0) return ATTN_ERR_BAD_SHAPE;
+    if (prod({B, Hq, (S + 63) / 64, 2}) > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+    if (misaligned(p, 16) || misaligned(v, 16) || misaligned(out, 16)) return ATTN_ERR_MISALIGNED;
+    if (overlap(out, no, p, np) || overlap(out, no, v, nv)) return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+attn::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
+                       int S, int D, float scale, int causal) {
+    attn::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.S = S;
+    a.D = D;
+    a.scale = scale;
+    a.causal = causal;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+                          int Hkv, int S, int D, float scale, int causal, void* stream) {
+    const attn_status st = check_fwd(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, 2);
+    if (st != ATTN_OK) return st;
+    return hip_status(attn::launch_fwd_bf16(fwd_args(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal),
+                                            (hipStream_t)stream));
+}
+
+attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse, int B, int Hq,
+                         int Hkv, int S, int D, float scale, int causal, void* stream) {
+    const attn_status st = check_fwd(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, 4);
+    if (st != ATTN_OK) return st;
+    return hip_status(attn::launch_fwd_f32(fwd_args(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal),
+                                           (hipStream_t)stream));
+}
+
+static attn_status qk_common(const void* q, const void* k, float* scores, int B, int Hq, int Hkv, int S, int D,
+                             void* stream, int esz) {
+    const attn_status st = check_qk(q, k, scores, B, Hq, Hkv, S, D, esz);
+    if (st != ATTN_OK) return st;
+    attn::QkArgs a;
+    a.q = q;
+    a.k = k;
+    a.scores = scores;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.S = S;
+    a.D = D;
+    return hip_status(esz == 2 ? attn::launch_qk_gemm_bf16(a, (hipStream_t)stream)
+                               : attn::launch_qk_gemm_f32(a, (hipStream_t)stream));
+}
+
+attn_status attn_qk_gemm_bf16(const void* q, const void* k, float* scores, int B, int Hq, int Hkv, int S, int D,
+                              void* stream) {
+    return qk_common(q, k, scores, B, Hq, Hkv, S, D, stream, 2);
+}
+
+attn_status attn_qk_gemm_f32(const float* q, const float* k, float* scores, int B, int Hq, int Hkv, int S, int D,
+                             void* stream) {
+    return qk_common(q, k, scores, B, Hq, Hkv, S, D, stream, 4);
+}
+
+static attn_status softmax_common(const float* scores, void* p, float* lse, int B, int H, int S, float scale,
+                                  int causal, void* stream, int esz) {
+    const attn_status st = check_softmax(scores, p, lse, B, H, S, scale, causal, esz);
+    if (st != ATTN_OK) return st;
+    attn::SoftmaxArgs a;
+    a.scores = scores;
+    a.p = p;
+    a.lse = lse;
+    a.B = B;
+    a.H = H;
+    a.S = S;
+    a.scale = scale;
+    a.causal = causal;
+    return hip_status(esz == 2 ? attn::launch_masked_softmax_bf16(a, (hipStream_t)stream)
+                               : attn::launch_masked_softmax_f32(a, (hipStream_t)stream));
+}
+
+attn_status attn_masked_softmax_bf16(const float* scores, void* p, float* lse, int B, int H, int S, float scale,
+                                     int causal, void* stream) {
+    return softmax_common(scores, p, lse, B, H, S, scale, causal, stream, 2);
+}
+
+attn_status attn_masked_softmax_f32(const float* scores, float* p, float* lse, int B, int H, int S, float scale,
+                                    int causal, void* stream) {
+    return softmax_common(scores, p, lse, B, H, S, scale, causal, stream, 4);
+}
+
+static attn_status pv_common(const void* p, const void* v, void* out, int B, int Hq, int Hkv, int S, int D,
+                             void* stream, int esz) {
+    const attn_status st = check_pv(p, v, out, B, Hq, Hkv, S, D, esz);
+    if (st != ATTN_OK) return st;
+    attn::PvArgs a;
+    a.p = p;
+    a.v = v;
+    a.out = out;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.S = S;
+    a.D = D;
+    return hip_status(esz == 2 ? attn::launch_pv_gemm_bf16(a, (hipStream_t)stream)
+                               : attn::launch_pv_gemm_f32(a, (hipStream_t)stream));
+}
+
+attn_status attn_pv_gemm_bf16(const void* p, const void* v, void* out, int B, int Hq, int Hkv, int S, int D,
+                              void* stream) {
+    return pv_common(p, v, out, B, Hq, Hkv, S, D, stream, 2);
+}
+
+attn_status attn_pv_gemm_f32(const float* p, const float* v, float* out, int B, int Hq, int Hkv, int S, int D,
+                             void* stream) {
+    return pv_common(p, v, out, B, Hq, Hkv, S, D, stream, 4);
+}
+
+size_t attn_scores_bytes(int B, int Hq, int S) {
+    const int64_t n = prod({B, Hq, S, S, 4});
+    return n < 0 ? 0 : (size_t)n;
+}
+
+size_t attn_probs_bytes(int B, int Hq, int S, int elem_bytes) {
+    if (elem_bytes != 2 && elem_bytes != 4) return 0;
+    const int64_t n = prod({B, Hq, S, S, elem_bytes});
+    return n < 0 ? 0 : (size_t)n;
+}
+
+const char* attn_status_str(attn_status s) {
+    switch (s) {
+        case ATTN_OK: return "ATTN_OK";
+        case ATTN_ERR_NULL_POINTER: return "ATTN_ERR_NULL_POINTER: a required pointer is NULL";
+        case ATTN_ERR_BAD_SHAPE: return "ATTN_ERR_BAD_SHAPE: a size < 1, Hq % Hkv != 0, or a size overflows";
+        case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: D must be 64 or 128 and causal 0 or 1";
+        case ATTN_ERR_BAD_SCALE: return "ATTN_ERR_BAD_SCALE: scale must be finite and > 0";
+        case ATTN_ERR_MISALIGNED: return "ATTN_ERR_MISALIGNED: tensors need 16-byte alignment (lse 4)";
+        case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS: an output overlaps an input";
+        case ATTN_ERR_HIP: return "ATTN_ERR_HIP: kernel launch failed";
+    }
+    return "unknown attn_status";
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

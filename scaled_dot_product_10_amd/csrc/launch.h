@@ -1,0 +1,52 @@
+// Internal launchers behind the C ABI (include/attn.h).  Arguments are
+// already validated by the caller; each launcher enqueues exactly one kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace attn {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;  // may be null
+    int B, Hq, Hkv, S, D;
+    float scale;  // > 0, finite
+    int causal;   // 0 or 1
+};
+
+struct QkArgs {
+    const void* q;
+    const void* k;
+    float* scores;
+    int B, Hq, Hkv, S, D;
+};
+
+struct SoftmaxArgs {
+    const float* scores;
+    void* p;
+    float* lse;  // may be null
+    int B, H, S;
+    float scale;
+    int causal;
+};
+
+struct PvArgs {
+    const void* p;
+    const void* v;
+    void* out;
+    int B, Hq, Hkv, S, D;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_qk_gemm_bf16(const QkArgs& a, hipStream_t stream);
+hipError_t launch_qk_gemm_f32(const QkArgs& a, hipStream_t stream);
+hipError_t launch_masked_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream);
+hipError_t launch_masked_softmax_f32(const SoftmaxArgs& a, hipStream_t stream);
+hipError_t launch_pv_gemm_bf16(const PvArgs& a, hipStream_t stream);
+hipError_t launch_pv_gemm_f32(const PvArgs& a, hipStream_t stream);
+
+}  // namespace attn

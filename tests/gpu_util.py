@@ -1,0 +1,61 @@
+"""Helpers for the GPU parity tests: host<->device transfer of generator
+tensors, row sampling and error statistics.  No attention arithmetic here."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+# spec tolerances: max-abs / mean-abs error of out against the fp64 oracle
+TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}
+# lse is not bounded by the pages; these bounds are derived in the design doc
+LSE_TOL = {"bf16": 1e-3, "f32": 1e-5}
+
+
+def dev(t, device="cuda"):
+    import torch
+
+    if t.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(t.f32)).to(device)
+
+
+def host(x) -> np.ndarray:
+    """Exact float64 image of a bf16/fp32 device tensor."""
+    return x.detach().float().cpu().numpy().astype(np.float64)
+
+
+def sample_rows(B, H, S, n_random, seed, tile=128):
+    """Flattened [B,H,S] row indices: first/last rows, tile edges and random rows."""
+    rng = np.random.default_rng(seed)
+    edge = sorted({0, 1, 2, 31, 32, 63, 64, tile - 1, tile, tile + 1, S // 2, S - 2, S - 1} & set(range(S)))
+    rows = []
+    for bh in sorted({0, B * H - 1, int(rng.integers(B * H))}):
+        rows += [bh * S + i for i in edge]
+    rows += list(rng.integers(0, B * H * S, n_random))
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+def errs(got, ref):
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
+    return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
+
+
+def report(name, **vals):
+    msg = " ".join(f"{k}={v:.3e}" if isinstance(v, float) else f"{k}={v}" for k, v in vals.items())
+    print(f"[{name}] {msg}", file=sys.stderr, flush=True)
+
+
+def check_close(name, got, ref, dtype, lse_got=None, lse_ref=None, lse_tol=None):
+    mx, mean = errs(got, ref)
+    tol_max, tol_mean = TOL[dtype]
+    vals = dict(max_abs=mx, mean_abs=mean)
+    if lse_got is not None:
+        vals["lse_max"] = errs(lse_got, lse_ref)[0]
+    report(name, **vals)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    assert mx <= tol_max, f"{name}: max abs err {mx:.3e} > {tol_max}"
+    assert mean <= tol_mean, f"{name}: mean abs err {mean:.3e} > {tol_mean}"
+    if lse_got is not None:
+        tol = LSE_TOL[dtype] if lse_tol is None else lse_tol
+        assert vals["lse_max"] <= tol, f"{name}: lse err {vals['lse_max']:.3e} > {tol:.3e}"

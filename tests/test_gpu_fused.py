@@ -1,0 +1,160 @@
+"""Fused forward (attn_fwd_bf16 / attn_fwd_f32) against the fp64 CPU oracle.
+
+Small shapes are compared element by element over the whole output; they span
+several 128-query and 64-key tiles and ragged tails.  The full workloads (the
+five measured configurations, in the launch configuration the bench times)
+are compared on sampled rows, which the oracle computes one at a time, plus
+properties checked over every row.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import gpu_util as G
+from scaled_dot_product_10_amd import api, inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+SMALL = [
+    (1, 1, 1, 1, 64), (1, 2, 2, 1, 128), (1, 1, 1, 3, 128), (1, 2, 1, 17, 64), (2, 4, 2, 127, 64),
+    (1, 3, 1, 129, 128), (1, 2, 2, 200, 128), (2, 2, 2, 256, 64), (1, 4, 1, 300, 128),
+    (1, 2, 2, 1000, 128), (1, 8, 8, 64, 128), (1, 1, 1, 640, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}H{}kv{}S{}D{}".format(*s))
+def test_small_full_compare(orc, shape, causal, dtype):
+    B, Hq, Hkv, S, D = shape
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, dtype, seed=1000 + S + D + Hq)
+    sc = 1.0 / math.sqrt(D)
+    out, lse = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    ref_o, ref_l = orc.attn_fwd(q.f32, k.f32, v.f32, sc, causal)
+    G.check_close(f"fwd {dtype} {shape} causal={causal}", G.host(out), ref_o, dtype, G.host(lse), ref_l)
+
+
+# ---------------------------------------------------------------------------
+# the measured workloads
+# ---------------------------------------------------------------------------
+_CACHE = {}
+
+
+def workload(name):
+    if name not in _CACHE:
+        c = inputs.CONFIGS[name]
+        q, k, v = inputs.make_qkv(c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], c["dtype"], c["seed"])
+        _CACHE.clear()  # keep one workload resident at a time
+        _CACHE[name] = (c, q, k, v, G.dev(q), G.dev(k), G.dev(v))
+    return _CACHE[name]
+
+
+@pytest.mark.parametrize("name,causal", [("C1", True), ("C2", True), ("C3", True), ("C3", False), ("C4", True),
+                                         ("C5", True)])
+def test_config(orc, name, causal):
+    c, q, k, v, dq, dk, dv = workload(name)
+    B, Hq, S, D = c["B"], c["Hq"], c["S"], c["D"]
+    sc = 1.0 / math.sqrt(D)
+    out, lse = api.fwd(dq, dk, dv, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    if name == "C1":
+        ref_o, ref_l = orc.attn_fwd(q.f32, k.f32, v.f32, sc, causal)
+        G.check_close(f"{name} causal={causal}", G.host(out), ref_o, c["dtype"], G.host(lse), ref_l)
+        return
+    rows = G.sample_rows(B, Hq, S, n_random=400, seed=c["seed"])
+    ref_o, ref_l = orc.attn_fwd(q.f32, k.f32, v.f32, sc, causal, rows=rows)
+    o = out.view(-1, D)[torch.from_numpy(rows).to(out.device)]
+    l = lse.view(-1)[torch.from_numpy(rows).to(out.device)]
+    G.check_close(f"{name} causal={causal} rows={rows.size}", G.host(o), ref_o, c["dtype"], G.host(l), ref_l)
+    # every row written and finite
+    assert bool(torch.isfinite(lse).all())
+    assert bool(torch.isfinite(out.float()).all())
+    if causal:
+        # row 0 sees key 0 only: out = v_0 bit for bit (p = 1, l = 1)
+        g = Hq // c["Hkv"]
+        v0 = dv[:, :, 0, :].repeat_interleave(g, dim=1)
+        assert torch.equal(out[:, :, 0, :], v0)
+
+
+def test_row0_bitwise_f32():
+    q, k, v = inputs.make_qkv(2, 4, 2, 70, 64, "f32", seed=77)
+    out, _ = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=True)
+    ref = torch.from_numpy(v.f32[:, :, 0, :]).repeat_interleave(2, dim=1)
+    assert torch.equal(out[:, :, 0, :].cpu(), ref)
+
+
+def test_deterministic_and_streams():
+    c, q, k, v, dq, dk, dv = workload("C2")
+    o1, l1 = api.fwd(dq, dk, dv, causal=True)
+    o2, l2 = api.fwd(dq, dk, dv, causal=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o3, l3 = api.fwd(dq, dk, dv, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_poisoned_outputs_fully_written():
+    q, k, v = inputs.make_qkv(2, 4, 1, 333, 128, "bf16", seed=78)
+    dq = G.dev(q)
+    out = torch.full_like(dq, float("nan"))
+    lse = torch.full((2, 4, 333), float("nan"), device=dq.device)
+    api.fwd(dq, G.dev(k), G.dev(v), causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(lse).all())
+
+
+def test_lse_optional(orc):
+    q, k, v = inputs.make_qkv(1, 2, 2, 130, 64, "bf16", seed=79)
+    out, lse = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=False, lse=False)
+    torch.cuda.synchronize()
+    assert lse is None
+    ref_o, _ = orc.attn_fwd(q.f32, k.f32, v.f32, 0.125, False)
+    G.check_close("fwd lse=None", G.host(out), ref_o, "bf16")
+
+
+def test_no_device_allocation():
+    c, q, k, v, dq, dk, dv = workload("C2")
+    out = torch.empty_like(dq)
+    lse = torch.empty(dq.shape[:3], device=dq.device, dtype=torch.float32)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(3):
+        api.fwd(dq, dk, dv, causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_logits(orc, dtype):
+    """Logits with standard deviation 8 (peaked softmax, big running-max jumps)."""
+    B, Hq, Hkv, S, D = 1, 2, 1, 500, 128
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, dtype, seed=80)
+    qs = inputs._finish(q.f32 * 8.0, dtype)  # exact: power-of-two scaling
+    out, lse = api.fwd(G.dev(qs), G.dev(k), G.dev(v), causal=True)
+    torch.cuda.synchronize()
+    sc = 1 / math.sqrt(D)
+    ref_o, ref_l = orc.attn_fwd(qs.f32, k.f32, v.f32, sc, True)
+    # lse is 1-Lipschitz in the logits (max norm): its error is bounded by the
+    # float32 dot-product error gamma_D * scale * sum|q_d k_d| (u = 2^-23 covers
+    # both the vector FMAs and the matrix cores), plus the exp2/log2 error
+    u = 2.0 ** -23
+    absdot = np.matmul(np.abs(qs.f32.astype(np.float64)),
+                       np.abs(np.repeat(k.f32, Hq // Hkv, axis=1).astype(np.float64)).transpose(0, 1, 3, 2))
+    lse_tol = D * u / (1 - D * u) * sc * float(absdot.max()) + G.LSE_TOL[dtype]
+    G.check_close(f"large logits {dtype}", G.host(out), ref_o, dtype, G.host(lse), ref_l, lse_tol=lse_tol)
