@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="seconds of untimed steps before the warmup steps (clock ramp-up)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -175,6 +177,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # Clock settle (untimed): the GPU needs a few hundred ms of sustained load
+    # before its clocks reach steady state; run the same step until then.
+    settle = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(20):
+            fused()
+        torch.cuda.synchronize()
+        settle += 20
     for _ in range(args.warmup):
         fused()
     torch.cuda.synchronize()
@@ -289,6 +300,7 @@ def main():
         "gpu": props.name,
         "cus": props.multi_processor_count,
         "timed_wall_s": round(wall, 4),
+        "settle_steps": settle,
     }
     print(json.dumps(line), flush=True)
 
