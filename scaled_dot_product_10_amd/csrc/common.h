@@ -23,6 +23,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// acc + lo + hi of two bf16 packed in one dword (v_dot2_f32_bf16 against 1.0, 1.0;
+// the products are exact).
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
 // 2^x on the transcendental unit; exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

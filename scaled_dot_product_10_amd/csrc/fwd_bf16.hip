@@ -10,33 +10,33 @@
 // section 4 of the ai-manual.ru tutorial, with the online softmax and causal
 // masking that the sketch leaves out.
 //
-// Work decomposition (gfx950, wave64, two workgroups per CU):
-//   workgroup = 4 waves = 128 queries of one (batch, head); wave w owns 32.
-//   Each loop step handles BN = 64 keys:
-//     S^T = K . Q^T    v_mfma_f32_32x32x16_bf16.  A = K rows read from LDS,
-//                      B = the wave's Q rows, held in VGPRs for the whole
-//                      loop.  In the 32x32 result lane l holds one query
-//                      (l % 32) and 16 keys, so row max / row sum are
-//                      in-lane plus one exchange with lane l ^ 32.
-//     online softmax   p = 2^(s*c - m*c), c = scale*log2(e).  m is only moved
-//                      when a row max exceeds it by more than 2^8 in p units
-//                      (p stays <= 256, far from float32 overflow), so the
-//                      rescale of O by 2^((m_old - m_new) c) is rare.
-//     O^T += V^T . P^T same MFMA.  B = P^T straight from the S^T accumulator
-//                      (converted to bf16).  A = V^T comes from the row-major
-//                      V tile through ds_read_b64_tr_b16, which hands each
-//                      lane 4 keys of one d; the keys it picks match the
-//                      order of the S^T accumulator rows.
+// Work decomposition (gfx950, wave64):
+//   workgroup = 8 waves = 256 queries of one (batch, head); wave w owns 32.
+//   The hardware puts waves w and w+4 on the same SIMD.
+//   For each tile of BN = 64 keys a wave runs two phases:
+//     M phase (matrix cores):  S(n+1)^T = K(n+1).Q^T and O^T += V(n)^T.P(n)^T,
+//                      32 v_mfma_f32_32x32x16_bf16 with their LDS reads.
+//     V phase (vector ALUs):   mask and row max of S(n), then
+//                      p = 2^(s c - m c) (c = scale*log2(e)), row sums, and
+//                      P(n) packed to bf16.
+//   Waves 0-3 run one phase ahead of waves 4-7, with a workgroup barrier
+//   after every phase, so on every SIMD one wave issues matrix products while
+//   its partner does the softmax: the matrix cores and the vector ALUs work
+//   at the same time instead of taking turns.
+//   S^T (not S) is computed so that lane l holds one query (l % 32) and 16
+//   keys: row max / row sum are in-lane plus one exchange with lane l ^ 32,
+//   and P^T is directly the B operand of the second product.  V^T comes from
+//   the row-major V tile through ds_read_b64_tr_b16, which hands each lane 4
+//   keys of one d, in the key order of the S^T accumulator rows.
+//   m is only moved when a row max exceeds it by more than 2^8 in p units
+//   (p stays <= 256, far from float32 overflow), so rescaling O is rare.
 //   Memory pipeline: K and V tiles go HBM -> LDS with global_load_lds_dwordx4
-//   (no register staging), double-buffered; K(n+2) and V(n+1) are in flight
-//   while tile n is computed, and one barrier per step publishes them.  The
-//   product S(n+1) = K(n+1).Q^T is issued before the softmax of tile n, so the
-//   matrix cores have independent work while the vector ALUs run the softmax.
-//   LDS rows are XOR-swizzled in 16-byte chunks so every operand read is
-//   free of bank conflicts.
+//   (no register staging), double-buffered, each in flight for two phases.
+//   LDS rows are XOR-swizzled in 16-byte chunks so every operand read is free
+//   of bank conflicts.
 //   Causal: key tiles past the workgroup's last query are never loaded, a
-//   wave skips the products of tiles past its own last query, and only tiles
-//   that straddle the diagonal (or the end of the sequence) apply the mask.
+//   wave skips the work of tiles past its own last query, and only tiles that
+//   straddle the diagonal (or the end of the sequence) apply the mask.
 //   Causal workgroups start with the longest query tiles.
 #include <type_traits>
 
@@ -46,10 +46,11 @@
 namespace attn {
 namespace {
 
-constexpr int BM = 128;   // queries per workgroup
-constexpr int BN = 64;    // keys per loop step
-constexpr int NT = 256;   // threads per workgroup
-constexpr float kRescaleLog2 = 8.0f;  // move m only when p would exceed 2^8
+constexpr int BM = 256;   // queries per workgroup
+constexpr int BN = 64;    // keys per tile
+constexpr int NW = 8;     // waves per workgroup (two per SIMD)
+constexpr int NT = NW * 64;
+constexpr float kMaxTileSum = 4096.0f;  // bound on one lane tile sum of p (so p <= 2^12)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -62,8 +63,7 @@ struct Params {
     float* lse;
     int Hq, Hkv, S, group, nq;
     uint32_t total;
-    float c;    // scale * log2(e), > 0
-    float thr;  // kRescaleLog2 / c: rescale threshold in raw score units
+    float c;  // scale * log2(e), > 0
 };
 
 // LDS tile layout: BN rows x D bf16, 16-byte chunks.  Chunk c of row r sits
@@ -72,7 +72,7 @@ template <int D>
 struct Tile {
     static constexpr int CPR = D / 8;                 // chunks per row
     static constexpr int BYTES = BN * D * 2;          // 16 KB (D=128) / 8 KB (D=64)
-    static constexpr int DMA_PER_WAVE = BYTES / 1024 / 4;
+    static constexpr int DMA_PER_WAVE = BYTES / 1024 / NW;
     // K: the 16 rows one operand read touches per 16-lane phase land on 16
     // different bank groups (rows of 128 bytes alternate bank halves).
     __device__ static int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
@@ -86,37 +86,67 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 }
 
 // One global_load_lds_dwordx4: 64 lanes x 16 bytes from global memory into 1 KB
-// of LDS at lds (wave-uniform), lane L filling bytes [16L, 16L+16).  Issued as
-// inline assembly so the compiler does not treat every later LDS read as
-// dependent on it; completion is awaited explicitly (s_waitcnt vmcnt(0)) before
-// the barrier that publishes the tile.  M0 is a reserved register that the
-// compiler loads right before each of its own uses, so setting it here is safe.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+// of LDS at lds (wave-uniform), lane L filling bytes [16L, 16L+16); lane L
+// fetches base + off (base wave-uniform, off per lane).  Issued as inline
+// assembly so the compiler does not treat every later LDS read as dependent on
+// it; completion is awaited explicitly (s_waitcnt vmcnt(0)) before the barrier
+// that publishes the tile.  M0 is a reserved register that the compiler loads
+// right before each of its own uses, so setting it here is safe.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory");
 }
 
-// Issue this wave's share of the DMA of one K or V tile (rows n0..n0+BN-1).
-// Each global_load_lds_dwordx4 fills 1 KB of LDS, lane L writing bytes
-// [16L, 16L+16) of it; the lane fetches whichever global chunk belongs at
-// that swizzled position.  Rows past the end of the sequence repeat row S-1
-// (those keys are masked, and their P is 0).
+// Per-lane source offsets of the DMA of one K or V tile.  Instruction i of
+// wave w fills LDS chunk positions p = (w*PER + i)*64 + lane; position p holds
+// chunk c = (p % CPR) ^ swizzle(r) of tile row r = p / CPR, so the lane fetches
+// byte offset r*2D + 16c from the tile's first row.
 template <int D, bool IS_V>
-__device__ __forceinline__ void dma_tile(const uint16_t* base, int n0, int S, char* tile, int wave, int lane) {
+struct DmaPlan {
     using T = Tile<D>;
+    uint32_t off[T::DMA_PER_WAVE];
+    __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
-        const int inst = wave * T::DMA_PER_WAVE + i;
-        const int p = inst * 64 + lane;
-        const int r = p / T::CPR;
-        const int c = (p % T::CPR) ^ (IS_V ? T::vswz(r) : T::kswz(r));
-        const int key = min(n0 + r, S - 1);
-        dma16(base + (int64_t)key * D + c * 8, lds_addr(tile) + inst * 1024);
+        for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+            const int p = (wave * T::DMA_PER_WAVE + i) * 64 + lane;
+            const int r = p / T::CPR;
+            const int c = (p % T::CPR) ^ (IS_V ? T::vswz(r) : T::kswz(r));
+            off[i] = (uint32_t)(r * D * 2 + c * 16);
+        }
     }
-}
+    // rows n0 .. n0+BN-1 of the head starting at base; rows past the end of
+    // the sequence repeat row S-1 (those keys are masked and their P is 0)
+    __device__ __forceinline__ void issue(const uint16_t* base, int n0, int S, char* tile, int wave) const {
+        const uint16_t* tb = base + (int64_t)n0 * D;
+        const uint32_t l0 = lds_addr(tile) + (uint32_t)(wave * T::DMA_PER_WAVE) * 1024u;
+        if (n0 + BN <= S) {
+#pragma unroll
+            for (int i = 0; i < T::DMA_PER_WAVE; ++i) dma16(tb, off[i], l0 + i * 1024);
+        } else {
+            const int last = S - 1 - n0;  // last valid row of this tile
+#pragma unroll
+            for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+                const int r = (int)(off[i] / (D * 2));
+                const uint32_t o = off[i] - (uint32_t)((r - min(r, last)) * D * 2);
+                dma16(tb, o, l0 + i * 1024);
+            }
+        }
+    }
+};
 
-__device__ __forceinline__ void wait_dma_and_barrier() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+// Workgroup barrier between phases.  Inline assembly so that the compiler adds
+// no fence of its own (its fence would wait for every outstanding load,
+// including the tile DMA that is meant to stay in flight across the barrier);
+// the "memory" clobber keeps LDS accesses from moving across it.  LDS reads
+// are drained first; with wait_dma, this wave's tile DMA as well.
+// The sched_barrier(0) fences keep the compiler from moving any instruction
+// (matrix products and exponentials included) from one phase into the next.
+__device__ __forceinline__ void phase_barrier(bool wait_dma) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (wait_dma)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ bf16x8 tr_read_pair(const char* p0, const char* p1) {
@@ -127,18 +157,20 @@ __device__ __forceinline__ bf16x8 tr_read_pair(const char* p0, const char* p1) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(Params p) {
+__global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     using T = Tile<D>;
     constexpr int KS = D / 16;  // k-steps of the Q.K^T product
     constexpr int DB = D / 32;  // 32-row blocks of O^T
     constexpr int ROWB = T::CPR * 16;  // bytes per tile row
     __shared__ __attribute__((aligned(1024))) char smem[4 * T::BYTES];
-    char* Kb[2] = {smem, smem + T::BYTES};
-    char* Vb[2] = {smem + 2 * T::BYTES, smem + 3 * T::BYTES};
+    // K buffers at [0, 2*BYTES), V buffers at [2*BYTES, 4*BYTES)
+    auto Kbuf = [&](int i) __attribute__((always_inline)) { return smem + (i & 1) * T::BYTES; };
+    auto Vbuf = [&](int i) __attribute__((always_inline)) { return smem + (2 + (i & 1)) * T::BYTES; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;  // 0: waves 0-3 (one phase ahead), 1: waves 4-7
     const int l32 = lane & 31;
     const int g = lane >> 5;
 
@@ -182,9 +214,13 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(Params p) {
     const int nend = CAUSAL ? min(ntiles, qlast / BN + 1) : ntiles;
 
     // ---- prologue: K(0), V(0), K(1) in flight while Q is loaded -------------
-    dma_tile<D, false>(kb, 0, S, Kb[0], wave, lane);
-    dma_tile<D, true>(vb, 0, S, Vb[0], wave, lane);
-    if (nend > 1) dma_tile<D, false>(kb, BN, S, Kb[1], wave, lane);
+    DmaPlan<D, false> kdma;
+    DmaPlan<D, true> vdma;
+    kdma.init(wave, lane);
+    vdma.init(wave, lane);
+    kdma.issue(kb, 0, S, Kbuf(0), wave);
+    vdma.issue(vb, 0, S, Vbuf(0), wave);
+    if (nend > 1) kdma.issue(kb, BN, S, Kbuf(1), wave);
 
     // Q operand (B of S^T = K.Q^T): query qi, d = 16*ks + 8*g .. +7.
     bf16x8 qreg[KS];
@@ -212,141 +248,218 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(Params p) {
     }
 
     const float c = p.c;
-    const float thr = p.thr;
     f32x16 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-    float mrow = -INFINITY;  // running reference max of raw scores for query qi
+    // Running reference max of query qi in scaled log2 units (m * c).  It
+    // starts at a finite -1e30 rather than -inf so that no exponent argument
+    // is ever inf - inf (this file is built without NaN semantics): on the
+    // first tile every unmasked p overflows to +inf, which the tile-sum check
+    // catches, and masked ones give 2^-inf = 0.
+    float mc = -1e30f;
     float lrow = 0.f;        // running sum of p over this lane's keys
+    f32x16 sacc[2];          // S^T of the tile in flight (two 32-key blocks)
+    bf16x8 pb[4];            // P^T of the tile in flight, bf16 (four 16-key blocks)
 
-    auto qk = [&](f32x16(&s)[2], const char* Kt) {
-        s[0] = f32x16{};
-        s[1] = f32x16{};
+    // S^T = K.Q^T for the tile in Kt.  Operands are read two products ahead;
+    // the scheduling fences stop the compiler from hoisting further reads
+    // (which would only raise register pressure).
+    auto qk = [&](const char* Kt) __attribute__((always_inline)) {
+        constexpr int NP = 2 * KS;  // products: (ks, sb) pairs
+        auto rd = [&](int i) __attribute__((always_inline)) { return *(const bf16x8*)(Kt + koff[i >> 1] + (i & 1) * 32 * ROWB); };
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
+        bf16x8 a0 = rd(0), a1 = rd(1);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                const bf16x8 a = *(const bf16x8*)(Kt + koff[ks] + sb * 32 * ROWB);
-                s[sb] = mfma32x32x16(a, qreg[ks], s[sb]);
+        for (int i = 0; i < NP; i += 2) {
+            bf16x8 n0, n1;
+            if (i + 2 < NP) {
+                n0 = rd(i + 2);
+                n1 = rd(i + 3);
             }
+            sacc[0] = mfma32x32x16(a0, qreg[i >> 1], sacc[0]);
+            sacc[1] = mfma32x32x16(a1, qreg[i >> 1], sacc[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            a0 = n0;
+            a1 = n1;
         }
     };
 
-    // Mask tile n's scores (diagonal / tail tiles only), take the row max and
-    // move the reference max m when the new max exceeds it by more than the
-    // threshold (then O and l are rescaled by 2^((m_old - m_new) c)).
-    auto rowmax = [&](f32x16(&s)[2], int n0, auto need_mask) {
-        if (need_mask) {
+    // O^T += V^T . P^T ; 16-key block kb16 uses rows 16*kb16 .. +15 of the tile.
+    // Same read-ahead scheme as qk: the next key block's operands are in flight
+    // while the current one is multiplied.
+    auto pv = [&](const char* Vt) __attribute__((always_inline)) {
+        auto rd = [&](int i) __attribute__((always_inline)) {  // product i = (kb16, db) = (i / DB, i % DB)
+            const char* base = Vt + voff[i % DB] + (i / DB) * 16 * ROWB;
+            return tr_read_pair(base, base + 8 * ROWB);
+        };
+        constexpr int NP = 4 * DB;
+        bf16x8 a0 = rd(0), a1 = rd(1);
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = n0 + sb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    if ((CAUSAL && key > qi) || key >= S) s[sb][r] = -INFINITY;
-                }
+        for (int i = 0; i < NP; i += 2) {
+            bf16x8 n0, n1;
+            if (i + 2 < NP) {
+                n0 = rd(i + 2);
+                n1 = rd(i + 3);
             }
-        }
-        float mt = s[0][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[0][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[1][r]);
-        return fmaxf(mt, __shfl_xor(mt, 32));
-    };
-    auto update_max = [&](float mt) {
-        const bool upd = mt > mrow + thr;
-        if (__builtin_amdgcn_ballot_w64(upd)) {
-            const float mnew = upd ? mt : mrow;
-            const float alpha = fast_exp2((mrow - mnew) * c);
-            lrow *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-            mrow = mnew;
+            oacc[i % DB] = mfma32x32x16(a0, pb[i / DB], oacc[i % DB]);
+            oacc[(i + 1) % DB] = mfma32x32x16(a1, pb[(i + 1) / DB], oacc[(i + 1) % DB]);
+            __builtin_amdgcn_sched_barrier(0);
+            a0 = n0;
+            a1 = n1;
         }
     };
 
-    // p = 2^(s c - m c) -> bf16 P^T operand; 16-key block kb16 = accumulator
-    // registers 8*(kb16&1).. of key block kb16>>1.
-    auto exp_pack = [&](f32x16(&s)[2], bf16x8(&pb)[4]) {
-        const float mc = mrow * c;
-        float psum = 0.f;
+    // p = 2^(s c - m c) for the current reference m -> bf16 P^T operand; returns
+    // this lane's sum of the bf16-rounded p (the weights the product uses).
+    // 16-key block kb16 = accumulator registers 8*(kb16&1).. of key block kb16>>1.
+    auto exp_pack = [&](float mref) __attribute__((always_inline)) {
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
 #pragma unroll
         for (int kb16 = 0; kb16 < 4; ++kb16) {
             const int sb = kb16 >> 1, hh = kb16 & 1;
             u32x4 w;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p0 = fast_exp2(fmaf(s[sb][hh * 8 + 2 * e], c, -mc));
-                const float p1 = fast_exp2(fmaf(s[sb][hh * 8 + 2 * e + 1], c, -mc));
-                psum += p0 + p1;
+                const float p0 = fast_exp2(fmaf(sacc[sb][hh * 8 + 2 * e], c, -mref));
+                const float p1 = fast_exp2(fmaf(sacc[sb][hh * 8 + 2 * e + 1], c, -mref));
                 w[e] = pack_bf16x2(p0, p1);
+                ps[e] = sum_bf16x2(w[e], ps[e]);
             }
             pb[kb16] = as_bf16x8(w);
         }
-        lrow += psum;
+        return (ps[0] + ps[1]) + (ps[2] + ps[3]);
     };
 
-    // O^T += V^T . P^T ; 16-key block kb16 uses rows 16*kb16 .. +15 of the tile
-    auto pv = [&](const bf16x8(&pb)[4], const char* Vt) {
+    // Softmax of tile n0 against the running reference max m.  Fast path: the
+    // exponentials with the current m.  The reference only has to keep p
+    // bounded: when some lane's tile sum exceeds 2^12 (or is inf/NaN, as on the
+    // first tile, where m = -inf) the slow path takes the tile's row max
+    // (exchanged between the two half-waves that share each query, so they keep
+    // one reference), moves m, rescales O and l by 2^((m_old - m_new) c) and
+    // redoes the exponentials, after which every p <= 1.
+    auto softmax_impl = [&](int n0, auto may_mask) __attribute__((always_inline)) {
+        if (may_mask && ((CAUSAL && n0 + BN - 1 > qwmin) || n0 + BN > S)) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+            for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-            for (int kb16 = 0; kb16 < 4; ++kb16) {
-                const char* base = Vt + voff[db] + kb16 * 16 * ROWB;
-                const bf16x8 a = tr_read_pair(base, base + 8 * ROWB);
-                oacc[db] = mfma32x32x16(a, pb[kb16], oacc[db]);
+                for (int r = 0; r < 16; ++r) {
+                    const int key = n0 + sb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                    if ((CAUSAL && key > qi) || key >= S) sacc[sb][r] = -INFINITY;
+                }
             }
         }
-    };
-
-    // Tiles whose every key is visible to every query of the workgroup and
-    // that lie fully inside the sequence: [0, nfull).
-    const int nfull = min(CAUSAL ? (m0 + 1) / BN : S / BN, S / BN);
-    // Step n is "fast" when tile n+1 is such a tile: then exp(n), S(n+1), PV(n)
-    // and max(n+1) form one branch-free block the scheduler can interleave.
-    const int nfast = max(0, min(nfull, nend) - 1);
-
-    // One step: on entry S(n) is in scur (masked, its max folded into m) and
-    // tiles n (K, V) and n+1 (K) are in LDS.
-    auto step = [&](int n, f32x16(&scur)[2], f32x16(&snext)[2], auto fast) {
-        const int n0 = n * BN;
-        if (n + 2 < nend) dma_tile<D, false>(kb, n0 + 2 * BN, S, Kb[n & 1], wave, lane);
-        if (n + 1 < nend) dma_tile<D, true>(vb, n0 + BN, S, Vb[(n + 1) & 1], wave, lane);
-        bf16x8 pb[4];
-        if (fast) {
-            exp_pack(scur, pb);
-            qk(snext, Kb[(n + 1) & 1]);
-            pv(pb, Vb[n & 1]);
-            update_max(rowmax(snext, n0 + BN, std::false_type{}));
-        } else {
-            const bool cur = !CAUSAL || n0 <= qwmax;
-            const bool nxt = n + 1 < nend && (!CAUSAL || n0 + BN <= qwmax);
-            if (cur) exp_pack(scur, pb);
-            if (nxt) qk(snext, Kb[(n + 1) & 1]);
-            if (cur) pv(pb, Vb[n & 1]);
-            if (nxt) update_max(rowmax(snext, n0 + BN, std::true_type{}));
+        float lt = exp_pack(mc);
+        if (__builtin_amdgcn_ballot_w64(!(lt <= kMaxTileSum))) {
+            float t[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t[i] = fmaxf(sacc[0][i], sacc[1][i]);
+#pragma unroll
+            for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+                for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[0]), __float_as_uint(t[0]), false, false);
+            const float mnew = fmaxf(mc, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c);
+            const float alpha = fast_exp2(mc - mnew);  // 0 on the first tile
+            lrow *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            mc = mnew;
+            lt = exp_pack(mc);
         }
-        wait_dma_and_barrier();
+        lrow += lt;
+    };
+    auto softmax = [&](int n0) __attribute__((always_inline)) { softmax_impl(n0, std::true_type{}); };
+
+    auto active = [&](int n) __attribute__((always_inline)) { return !CAUSAL || n * BN <= qwmax; };
+
+    phase_barrier(true);
+
+    // M(n), n >= 0: S(n+1) = K(n+1).Q^T and O += P(n).V(n) as one software
+    // pipeline of 2*KS + 4*DB products whose LDS operands are read AHEAD
+    // products in advance (the scheduling fences stop the compiler from
+    // hoisting reads further, which would only cost registers).  One code
+    // path: for the last tile the S(n+1) product reads the (stale, in-bounds)
+    // other K buffer and its result is never used.
+    auto mphase = [&](int n) __attribute__((always_inline)) {
+        if (!active(n)) return;
+        constexpr int NQK = 2 * KS, NPV = 4 * DB, NP = NQK + NPV, AHEAD = 4;
+        const char* Kt = Kbuf(n + 1);
+        const char* Vt = Vbuf(n);
+        auto rd = [&](int i) __attribute__((always_inline)) {
+            if (i < NQK) return *(const bf16x8*)(Kt + koff[i >> 1] + (i & 1) * 32 * ROWB);
+            const int j = i - NQK;  // (kb16, db) = (j / DB, j % DB)
+            const char* base = Vt + voff[j % DB] + (j / DB) * 16 * ROWB;
+            return tr_read_pair(base, base + 8 * ROWB);
+        };
+        __builtin_amdgcn_s_setprio(1);
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
+        bf16x8 buf[AHEAD];
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) buf[i] = rd(i);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const bf16x8 a = buf[i % AHEAD];
+            if (i + AHEAD < NP) buf[i % AHEAD] = rd(i + AHEAD);
+            if (i < NQK) {
+                sacc[i & 1] = mfma32x32x16(a, qreg[i >> 1], sacc[i & 1]);
+            } else {
+                const int j = i - NQK;
+                oacc[j % DB] = mfma32x32x16(a, pb[j / DB], oacc[j % DB]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // V(n): softmax of tile n (from S(n) of the previous M phase)
+    auto vphase = [&](int n) __attribute__((always_inline)) {
+        if (active(n)) softmax(n * BN);
+    };
+    // DMA of K(k+1) and V(k) at the start of phase 2k (k >= 1)
+    auto dma_step = [&](int k) __attribute__((always_inline)) {
+        if (k + 1 < nend) kdma.issue(kb, (k + 1) * BN, S, Kbuf(k + 1), wave);
+        if (k < nend) vdma.issue(vb, k * BN, S, Vbuf(k), wave);
     };
 
-    wait_dma_and_barrier();
-    f32x16 s0[2], s1[2];
-    qk(s0, Kb[0]);
-    update_max(rowmax(s0, 0, std::true_type{}));
-    // fast steps in pairs (keeps s0 as the current buffer at every even n),
-    // then the remaining steps on the general path
-    int n = 0;
-    for (; n + 1 < nfast; n += 2) {
-        step(n, s0, s1, std::true_type{});
-        step(n + 1, s1, s0, std::true_type{});
-    }
-    for (; n < nend; n += 2) {
-        step(n, s0, s1, std::false_type{});
-        if (n + 1 < nend) step(n + 1, s1, s0, std::false_type{});
+    // Phase schedule (barrier after every phase; odd phases also wait for the
+    // tile DMA started at the preceding even phase):
+    //   phase       0      2n+1    2n+2    ...  2nend+1
+    //   group 0   M(-1)    V(n)    M(n)         -
+    //   group 1     -      M(n-1)  V(n)         M(nend-1)
+    // with M(n) and V(n) as above, so group 0 runs one phase ahead and on every
+    // SIMD one wave issues matrix products while the other runs the softmax.
+    // K(m) is read in phases 2m and 2m+1, V(m) in phases 2m+2 and 2m+3.  The
+    // DMA of K(k+1) and V(k) starts at phase 2k into the buffers of K(k-1) and
+    // V(k-2), whose last readers finished in phase 2k-1, and is awaited before
+    // the barrier that ends phase 2k+1.
+    if (grp == 0) {
+        qk(Kbuf(0));
+        phase_barrier(false);
+        for (int n = 0; n < nend; ++n) {
+            vphase(n);
+            phase_barrier(true);
+            dma_step(n + 1);
+            mphase(n);
+            phase_barrier(false);
+        }
+        phase_barrier(true);
+    } else {
+        phase_barrier(false);
+        qk(Kbuf(0));
+        phase_barrier(true);
+        for (int n = 0; n < nend; ++n) {
+            dma_step(n + 1);
+            vphase(n);
+            phase_barrier(false);
+            mphase(n);
+            phase_barrier(true);
+        }
     }
 
     // ---- epilogue: O / l, lse ------------------------------------------------
-    const float ltot = lrow + __shfl_xor(lrow, 32);
+    const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
+    const float ltot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
     if (qi < S) {
         const float inv = 1.0f / ltot;
         uint16_t* orow = p.out + (row0 + qi) * D;
@@ -360,7 +473,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(Params p) {
                 *(u32x2*)(orow + d0) = w;
             }
         }
-        if (p.lse && g == 0) p.lse[row0 + qi] = (mrow * c + __log2f(ltot)) * kLn2;
+        if (p.lse && g == 0) p.lse[row0 + qi] = (mc + __log2f(ltot)) * kLn2;
     }
 }
 
@@ -387,7 +500,6 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     prm.nq = (a.S + BM - 1) / BM;
     prm.total = (uint32_t)((int64_t)a.B * a.Hq * prm.nq);
     prm.c = a.scale * kLog2e;
-    prm.thr = kRescaleLog2 / prm.c;
     if (a.D == 128) return a.causal ? launch<128, true>(prm, stream) : launch<128, false>(prm, stream);
     return a.causal ? launch<64, true>(prm, stream) : launch<64, false>(prm, stream);
 }

@@ -8,8 +8,12 @@ import numpy as np
 
 # spec tolerances: max-abs / mean-abs error of out against the fp64 oracle
 TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}
-# lse is not bounded by the pages; these bounds are derived in the design doc
-LSE_TOL = {"bf16": 1e-3, "f32": 1e-5}
+# lse is not bounded by the pages.  The bf16 kernels normalise by the sum of
+# the bf16-rounded weights they actually apply (so out is an exact convex
+# combination of v rows and lse matches out's normalisation); each rounded
+# weight is within 2^-8 of the exact one, relatively, so l is too and lse is
+# within ln(1 + 2^-8) < 3.9e-3 of the exact value, plus float32 rounding.
+LSE_TOL = {"bf16": 4e-3, "f32": 1e-5}
 
 
 def dev(t, device="cuda"):
