@@ -33,7 +33,7 @@ METRIC = "fused causal attn fwd TFLOP/s + % bf16 MFMA peak (B4 H16 S4096 D128)"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PROFILE = ROOT / "profiles" / "fwd_bf16_B4H16S4096D128_causal.md"
-KERNEL_SOURCES = ["fwd_bf16.hip", "kv_tile.h", "common.h"]
+KERNEL_SOURCES = ["fwd_bf16.hip", "common.h"]
 
 
 def attn_flops(B, H, S, D, causal):

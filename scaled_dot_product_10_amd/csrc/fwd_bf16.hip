@@ -63,8 +63,12 @@ struct Params {
     float* lse;
     int Hq, Hkv, S, group, nq;
     uint32_t total;
-    float c;  // scale * log2(e), > 0
+    uint32_t hgrp;  // causal: heads whose tiles one XCD runs together (0: plain order)
+    float c;        // scale * log2(e), > 0
 };
+
+// Workgroups one XCD holds at once: 32 CUs per XCD, one 8-wave workgroup per CU.
+constexpr int kSlotsPerXcd = 32;
 
 // LDS tile layout: BN rows x D bf16, 16-byte chunks.  Chunk c of row r sits
 // at chunk position r*CPR + (c ^ swizzle(r)).
@@ -177,14 +181,18 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     const uint32_t L = xcd_remap(blockIdx.x, p.total);
     int bh, tile;
     if (CAUSAL) {
-        // tile-major within each XCD's range: the longest tiles of every head first
-        const uint32_t per = p.total / 8u;
-        const uint32_t heads_here = per / (uint32_t)p.nq;
-        if (blockIdx.x < per * 8u && heads_here > 0 && per % (uint32_t)p.nq == 0) {
-            const uint32_t base = L - L % per;
+        if (p.hgrp > 0 && blockIdx.x < p.total / 8u * 8u) {
+            // Each XCD's range is cut into groups of hgrp heads whose tiles
+            // together fill the XCD; inside a group the longest tiles go
+            // first.  All tiles of a group start together and read the same
+            // K/V tiles in step, and the next group's long tiles take the CUs
+            // its short tiles free, so every CU ends up with the same work.
+            const uint32_t per = p.total / 8u;
             const uint32_t loc = L % per;
-            tile = p.nq - 1 - (int)(loc / heads_here);
-            bh = (int)(base / (uint32_t)p.nq + loc % heads_here);
+            const uint32_t gsz = p.hgrp * (uint32_t)p.nq;
+            const uint32_t r = loc % gsz;
+            tile = p.nq - 1 - (int)(r / p.hgrp);
+            bh = (int)((L - loc) / (uint32_t)p.nq + (loc / gsz) * p.hgrp + r % p.hgrp);
         } else {
             bh = (int)(L / (uint32_t)p.nq);
             tile = p.nq - 1 - (int)(L % (uint32_t)p.nq);
@@ -500,6 +508,15 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     prm.nq = (a.S + BM - 1) / BM;
     prm.total = (uint32_t)((int64_t)a.B * a.Hq * prm.nq);
     prm.c = a.scale * kLog2e;
+    prm.hgrp = 0;
+    const uint32_t per = prm.total / 8u;
+    if (per > 0 && per % (uint32_t)prm.nq == 0) {
+        const uint32_t heads_here = per / (uint32_t)prm.nq;
+        uint32_t g = (uint32_t)(kSlotsPerXcd / prm.nq > 1 ? kSlotsPerXcd / prm.nq : 1);
+        if (g > heads_here) g = heads_here;
+        while (heads_here % g) --g;
+        prm.hgrp = g;
+    }
     if (a.D == 128) return a.causal ? launch<128, true>(prm, stream) : launch<128, false>(prm, stream);
     return a.causal ? launch<64, true>(prm, stream) : launch<64, false>(prm, stream);
 }
