@@ -70,7 +70,7 @@ typedef enum attn_status {
     ATTN_ERR_NULL_POINTER = 1, /* a required pointer is NULL                          */
     ATTN_ERR_BAD_SHAPE = 2,    /* a size < 1, Hq % Hkv != 0, or a size overflows      */
     ATTN_ERR_UNSUPPORTED = 3,  /* D not in {64, 128}, or causal not in {0, 1}         */
-    ATTN_ERR_BAD_SCALE = 4,    /* scale is NaN or infinite                            */
+    ATTN_ERR_BAD_SCALE = 4,    /* scale is not finite, or not > 0                     */
     ATTN_ERR_MISALIGNED = 5,   /* a tensor pointer breaks the alignment rule          */
     ATTN_ERR_ALIAS = 6,        /* an output overlaps an input                         */
     ATTN_ERR_HIP = 7           /* the HIP launch failed; see attn_last_hip_error()    */
