@@ -43,6 +43,20 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& x) { return __builtin_bit_cast(bf16x8, x); }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Two ds_read_b64_tr_b16 (LDS, bf16 transposed): within each 16-lane group,
+// lane j addresses 4 consecutive bf16 of one row (4 rows x 16 columns per
+// group) and receives one column of those 4 rows.  p0 gives k-slots 0-3 of
+// an MFMA operand, p1 k-slots 4-7.
+__device__ __forceinline__ bf16x8 tr_read_pair(const void* p0, const void* p1) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1);
+    const short __attribute__((ext_vector_type(8))) x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, x);
+}
+
 // Workgroups are dealt round-robin over the chip's 8 XCDs (each with its own
 // L2).  Map the hardware id so that a contiguous range of logical ids runs
 // on one XCD: logical neighbours (tiles of one head) then share that L2.

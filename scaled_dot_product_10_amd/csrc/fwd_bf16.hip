@@ -52,9 +52,6 @@ constexpr int NW = 8;     // waves per workgroup (two per SIMD)
 constexpr int NT = NW * 64;
 constexpr float kMaxTileSum = 4096.0f;  // bound on one lane tile sum of p (so p <= 2^12)
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
 struct Params {
     const uint16_t* q;
     const uint16_t* k;
@@ -151,13 +148,6 @@ __device__ __forceinline__ void phase_barrier(bool wait_dma) {
     else
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ __forceinline__ bf16x8 tr_read_pair(const char* p0, const char* p1) {
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1);
-    const short __attribute__((ext_vector_type(8))) x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, x);
 }
 
 template <int D, bool CAUSAL>

@@ -8,7 +8,6 @@
 // The bfloat16 products use the same 32x32x16 MFMA as the fused kernel.  The
 // float32 variants run a plain LDS-tiled vector-ALU matrix product.
 #include "common.h"
-#include "kv_tile.h"
 #include "launch.h"
 
 namespace attn {
@@ -17,12 +16,17 @@ namespace {
 // ---------------------------------------------------------------------------
 // Step 1, bfloat16: scores[bh][i][j] = sum_d q[bh][i][d] k[bkv][j][d], float32.
 // 128 x 128 output tile per workgroup; wave (wi, wj) owns 64 x 64 = 2 x 2
-// MFMA blocks.  A = q rows (i = lane % 32), B = k rows (j = lane % 32), both
-// read straight from global memory (each row is reused by two waves through
-// the caches).  A store of one accumulator register writes 32 consecutive j
-// of two rows (128 bytes each).
+// MFMA blocks.  The 128-row Q and K tiles are loaded whole rows at a time
+// (D/8 lanes per row, so every load instruction covers whole cache lines)
+// into swizzled LDS, from which A = k rows (j = lane % 32) and B = q rows
+// (i = lane % 32) are read; a lane's accumulators then hold runs of 4
+// consecutive keys of one query.  The operand area is then reused: each wave
+// passes its 32 x 64 half-blocks through a private part of it and stores them
+// row by row, 16 lanes writing one row's 256 contiguous bytes, 16 bytes each,
+// so the score stores also cover whole cache lines.
 // ---------------------------------------------------------------------------
 constexpr int QK_T = 128;
+constexpr int QK_STAGE_LD = 68;  // floats per staged row: 64 keys + 4 (spreads rows over the banks)
 
 struct QkParams {
     const uint16_t* q;
@@ -35,6 +39,14 @@ struct QkParams {
 template <int D>
 __global__ __launch_bounds__(256) void qk_gemm_bf16_kernel(QkParams p) {
     constexpr int KS = D / 16;
+    constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    constexpr int LCH = QK_T * CPR / 256;       // chunks per thread per operand tile
+    constexpr int TILE = QK_T * D;              // elements per operand tile
+    constexpr int STAGE_BYTES = 4 * 32 * QK_STAGE_LD * 4;
+    constexpr int SMEM = 2 * TILE * 2 > STAGE_BYTES ? 2 * TILE * 2 : STAGE_BYTES;
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    uint16_t* Qs = (uint16_t*)smem;
+    uint16_t* Ks = Qs + TILE;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g = lane >> 5;
     const uint32_t L = xcd_remap(blockIdx.x, p.total);
@@ -44,48 +56,85 @@ __global__ __launch_bounds__(256) void qk_gemm_bf16_kernel(QkParams p) {
     const int ti = rem / p.nt, tj = rem % p.nt;
     const int b = bh / p.Hq, h = bh % p.Hq, kvh = h / p.group;
     const int S = p.S;
-    const uint16_t* qb = p.q + (int64_t)bh * S * D;
-    const uint16_t* kb = p.k + ((int64_t)b * p.Hkv + kvh) * S * D;
+    const uint16_t* qb = p.q + ((int64_t)bh * S + ti * QK_T) * D;
+    const uint16_t* kb = p.k + (((int64_t)b * p.Hkv + kvh) * S + tj * QK_T) * D;
+    // chunk c of row r sits at chunk position c ^ swz(r): the 16 rows one
+    // operand read touches land on different banks
+    auto swz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+    {
+        u32x4 rq[LCH], rk[LCH];
+#pragma unroll
+        for (int i = 0; i < LCH; ++i) {
+            const int c = tid + 256 * i, r = c / CPR, col = (c % CPR) * 8;
+            rq[i] = ti * QK_T + r < S ? *(const u32x4*)(qb + r * D + col) : u32x4{0, 0, 0, 0};
+            rk[i] = tj * QK_T + r < S ? *(const u32x4*)(kb + r * D + col) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < LCH; ++i) {
+            const int c = tid + 256 * i, r = c / CPR, pos = r * D + (((c % CPR) ^ swz(r)) * 8);
+            *(u32x4*)(Qs + pos) = rq[i];
+            *(u32x4*)(Ks + pos) = rk[i];
+        }
+    }
+    __syncthreads();
     const int ib = ti * QK_T + (wave >> 1) * 64;
     const int jb = tj * QK_T + (wave & 1) * 64;
+    const int rq0 = (wave >> 1) * 64 + l32, rk0 = (wave & 1) * 64 + l32;
 
     f32x16 acc[2][2];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
-
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         bf16x8 a[2], bb[2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            const int i = ib + x * 32 + l32;
-            const int j = jb + x * 32 + l32;
-            u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
-            if (i < S) va = *(const u32x4*)(qb + (int64_t)i * D + ks * 16 + g * 8);
-            if (j < S) vb = *(const u32x4*)(kb + (int64_t)j * D + ks * 16 + g * 8);
-            a[x] = as_bf16x8(va);
-            bb[x] = as_bf16x8(vb);
+            const int rq = rq0 + 32 * x, rk = rk0 + 32 * x;
+            a[x] = *(const bf16x8*)(Qs + rq * D + (((2 * ks + g) ^ swz(rq)) * 8));
+            bb[x] = *(const bf16x8*)(Ks + rk * D + (((2 * ks + g) ^ swz(rk)) * 8));
         }
+        // acc[x][y] = K-block y . Q-block x^T: lane l holds query ib + 32x + l % 32
+        // and keys jb + 32y + 8(r/4) + 4(l/32) + r%4 in accumulator r.
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int y = 0; y < 2; ++y) acc[x][y] = mfma32x32x16(a[x], bb[y], acc[x][y]);
+            for (int y = 0; y < 2; ++y) acc[x][y] = mfma32x32x16(bb[y], a[x], acc[x][y]);
     }
+    __syncthreads();  // operand tiles consumed; their space now stages the output
 
+    float* st = (float*)smem + wave * 32 * QK_STAGE_LD;
     float* sb = p.scores + (int64_t)bh * S * S;
+    const bool full = jb + 64 <= S && (S & 3) == 0;
+    const int rr = lane >> 4;        // row within a group of 4 staged rows
+    const int cc = (lane & 15) * 4;  // first of the lane's 4 keys
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-            const int j = jb + y * 32 + l32;
+        for (int y = 0; y < 2; ++y)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = ib + x * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                if (i < S && j < S) __builtin_nontemporal_store(acc[x][y][r], sb + (int64_t)i * S + j);
+            for (int q4 = 0; q4 < 4; ++q4)
+                *(f32x4*)(st + l32 * QK_STAGE_LD + y * 32 + q4 * 8 + g * 4) =
+                    f32x4{acc[x][y][4 * q4], acc[x][y][4 * q4 + 1], acc[x][y][4 * q4 + 2], acc[x][y][4 * q4 + 3]};
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int r = 4 * t + rr;
+            const int i = ib + x * 32 + r;
+            const f32x4 v = *(const f32x4*)(st + r * QK_STAGE_LD + cc);
+            if (i < S) {
+                float* dst = sb + (int64_t)i * S + jb + cc;
+                if (full) {
+                    __builtin_nontemporal_store(v, (f32x4*)dst);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (jb + cc + e < S) __builtin_nontemporal_store(v[e], dst + e);
+                }
             }
         }
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -279,9 +328,12 @@ __global__ __launch_bounds__(256) void softmax_rows_general_kernel(SmParams p) {
 // ---------------------------------------------------------------------------
 // Step 5, bfloat16: out[bh][i][d] = sum_j p[bh][i][j] v[bkv][j][d].
 // Computed as out^T = V^T . P^T on the 32x32x16 MFMA, 128 queries per
-// workgroup (32 per wave), 64 keys per step: V tiles are staged transposed in
-// LDS (natural key order), P rows are read straight from global memory as
-// the B operand (8 consecutive keys of one query per lane).
+// workgroup (32 per wave), 64 keys per step.  Both tiles are read from global
+// memory whole rows at a time (8 lanes per 128-byte P row segment, D/8 lanes
+// per V row), which keeps every load instruction on whole cache lines, and
+// pass through LDS: P rows as they are (the B operand is 8 consecutive keys
+// of one query), V rows swizzled and read back transposed.  The next step's
+// tiles are in flight in registers while a step multiplies.
 // ---------------------------------------------------------------------------
 constexpr int PV_BM = 128, PV_BN = 64;
 
@@ -296,8 +348,11 @@ struct PvParams {
 template <int D, bool ALIGNED>
 __global__ __launch_bounds__(256, 2) void pv_gemm_bf16_kernel(PvParams p) {
     constexpr int DB = D / 32;
-    using VT = VTile<D, PV_BN, 256, false>;
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VT::VPAD];
+    constexpr int PPAD = PV_BN + 8;
+    constexpr int CPR = D / 8;                   // 16-byte chunks per V row
+    constexpr int VCH = PV_BN * CPR / 256;       // V chunks per thread
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[PV_BN * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Ps[PV_BM * PPAD];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g = lane >> 5;
     const uint32_t L = xcd_remap(blockIdx.x, p.total);
@@ -306,44 +361,72 @@ __global__ __launch_bounds__(256, 2) void pv_gemm_bf16_kernel(PvParams p) {
     const int b = bh / p.Hq, h = bh % p.Hq, kvh = h / p.group;
     const int S = p.S;
     const int qi = tile * PV_BM + wave * 32 + l32;
-    const uint16_t* prow = p.p + ((int64_t)bh * S + (qi < S ? qi : 0)) * S;
+    const uint16_t* pbase = p.p + ((int64_t)bh * S + tile * PV_BM) * S;
     const uint16_t* vb = p.v + ((int64_t)b * p.Hkv + kvh) * S * D;
-
-    f32x16 oacc[DB];
+    auto vswz = [](int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+    u32x4 pr[4], vr[VCH];
+    auto load = [&](int n) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-    VT vt;
-    const int ntiles = (S + PV_BN - 1) / PV_BN;
-    for (int n = 0; n < ntiles; ++n) {
-        const int n0 = n * PV_BN;
-        vt.load(vb, n0, S, tid);
-        bf16x8 pb[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int j0 = n0 + kb * 16 + g * 8;
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i, r = c >> 3, key = n * PV_BN + (c & 7) * 8;
             u32x4 w = {0, 0, 0, 0};
-            if (qi < S) {
+            if (tile * PV_BM + r < S) {
+                const uint16_t* src = pbase + (int64_t)r * S + key;
                 if (ALIGNED) {
-                    if (j0 < S) w = *(const u32x4*)(prow + j0);
+                    if (key < S) w = *(const u32x4*)src;
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const uint32_t x = (j0 + e < S) ? prow[j0 + e] : 0u;
+                        const uint32_t x = (key + e < S) ? src[e] : 0u;
                         w[e >> 1] |= (e & 1) ? (x << 16) : x;
                     }
                 }
             }
-            pb[kb] = as_bf16x8(w);
+            pr[i] = w;
         }
-        __syncthreads();  // previous tile consumed
-        vt.store(Vt, tid);
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int c = tid + 256 * i, key = n * PV_BN + c / CPR;
+            vr[i] = key < S ? *(const u32x4*)(vb + (int64_t)key * D + (c % CPR) * 8) : u32x4{0, 0, 0, 0};
+        }
+    };
+    int voff[DB];  // transposed read: lane j of 16-lane group G takes rows 8(G/2) + j/4 (+4),
+                   // d = 32db + 16(G%2) + 4(j%4) .. +3
+    {
+        const int G = lane >> 4, j = lane & 15;
+        const int r = 8 * (G >> 1) + (j >> 2);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
+            const int d0 = db * 32 + (G & 1) * 16 + 4 * (j & 3);
+            voff[db] = r * D + (((d0 >> 3) ^ vswz(r)) * 8) + (d0 & 7);
+        }
+    }
+    f32x16 oacc[DB];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const bf16x8 a = *(const bf16x8*)(Vt + (db * 32 + l32) * VT::VPAD + kb * 16 + g * 8);
-                oacc[db] = mfma32x32x16(a, pb[kb], oacc[db]);
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    const int ntiles = (S + PV_BN - 1) / PV_BN;
+    load(0);
+    for (int n = 0; n < ntiles; ++n) {
+        __syncthreads();  // previous tile consumed
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i;
+            *(u32x4*)(Ps + (c >> 3) * PPAD + (c & 7) * 8) = pr[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int c = tid + 256 * i, r = c / CPR;
+            *(u32x4*)(Vs + r * D + (((c % CPR) ^ vswz(r)) * 8)) = vr[i];
+        }
+        __syncthreads();
+        if (n + 1 < ntiles) load(n + 1);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 bb = *(const bf16x8*)(Ps + (wave * 32 + l32) * PPAD + kb * 16 + g * 8);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const uint16_t* base = Vs + voff[db] + kb * 16 * D;
+                oacc[db] = mfma32x32x16(tr_read_pair(base, base + 4 * D), bb, oacc[db]);
             }
         }
     }
