@@ -16,6 +16,11 @@ profiling; each function's C counterpart states the definition it writes out):
 * ``qk_scores``  -- step 1 of that pipeline (q k^T, unscaled).
 * ``masked_softmax`` -- steps 2-4 (scale, mask with -inf, softmax).
 * ``pv``         -- step 5 (attn v).
+* ``attn_bwd`` (with ``attn_bwd_rows`` / ``attn_bwd_keys`` for sampled rows)
+  -- dq, dk, dv: the chain-rule derivative of ``attn_fwd`` for a given
+  gradient of its output (no gradient reaches lse).  The pages only warn
+  that the flash backward is easy to get wrong (ai-manual.ru tutorial,
+  section 6).
 
 Every function is pinned by tests in ``tests/test_oracle_pins.py`` against
 closed forms, invariants, hand-derived fixtures and independent library
@@ -74,6 +79,14 @@ class Oracle:
         L.oracle_pv_rows.restype = ctypes.c_int
         L.oracle_pv_rows.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _ptr, _i64, _ptr,
                                      ctypes.c_int]
+        L.oracle_attn_bwd_rows.restype = ctypes.c_int
+        L.oracle_attn_bwd_rows.argtypes = [_ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64,
+                                           ctypes.c_double, ctypes.c_int, _ptr, _i64, _ptr, _ptr,
+                                           _ptr, ctypes.c_int]
+        L.oracle_attn_bwd_keys.restype = ctypes.c_int
+        L.oracle_attn_bwd_keys.argtypes = [_ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64,
+                                           ctypes.c_double, ctypes.c_int, _ptr, _ptr, _ptr, _i64,
+                                           _ptr, _ptr, ctypes.c_int]
         L.oracle_plant_id.restype = ctypes.c_int
         L.oracle_plant_id.argtypes = []
 
@@ -171,6 +184,58 @@ class Oracle:
                                      self._threads(nthreads))
         self._check(rc, "oracle_pv_rows")
         return out.reshape(B, Hq, S, D) if rows is None else out
+
+
+    # -- backward -----------------------------------------------------------
+    def _bwd_args(self, q, k, v, dout):
+        q, k, v, dout = self._f32(q), self._f32(k), self._f32(v), self._f32(dout)
+        B, Hq, S, D = q.shape
+        Hkv = k.shape[1]
+        assert k.shape == (B, Hkv, S, D) and v.shape == k.shape and dout.shape == q.shape
+        return q, k, v, dout, (B, Hq, Hkv, S, D)
+
+    def attn_bwd_rows(self, q, k, v, dout, scale: float, causal: bool, rows=None, nthreads=None):
+        """Pass 1 for query rows (indices into the flattened ``[B,Hq,S]``):
+        lse, delta ``[n]`` and dq ``[n, D]``."""
+        q, k, v, dout, (B, Hq, Hkv, S, D) = self._bwd_args(q, k, v, dout)
+        r = self._rows(rows, B * Hq * S)
+        lse = np.empty((r.size,), np.float64)
+        delta = np.empty((r.size,), np.float64)
+        dq = np.empty((r.size, D), np.float64)
+        rc = self.lib.oracle_attn_bwd_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                           dout.ctypes.data, B, Hq, Hkv, S, D, float(scale),
+                                           int(bool(causal)), r.ctypes.data, r.size,
+                                           lse.ctypes.data, delta.ctypes.data, dq.ctypes.data,
+                                           self._threads(nthreads))
+        self._check(rc, "oracle_attn_bwd_rows")
+        return lse, delta, dq
+
+    def attn_bwd_keys(self, q, k, v, dout, scale: float, causal: bool, lse_all, delta_all,
+                      keys=None, nthreads=None):
+        """Pass 2 for key rows (indices into the flattened ``[B,Hkv,S]``):
+        dk, dv ``[n, D]``.  lse_all, delta_all: pass 1 over every query row."""
+        q, k, v, dout, (B, Hq, Hkv, S, D) = self._bwd_args(q, k, v, dout)
+        la = np.ascontiguousarray(lse_all, np.float64).reshape(-1)
+        da = np.ascontiguousarray(delta_all, np.float64).reshape(-1)
+        assert la.size == B * Hq * S and da.size == la.size
+        r = self._rows(keys, B * Hkv * S)
+        dk = np.empty((r.size, D), np.float64)
+        dv = np.empty((r.size, D), np.float64)
+        rc = self.lib.oracle_attn_bwd_keys(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                           dout.ctypes.data, B, Hq, Hkv, S, D, float(scale),
+                                           int(bool(causal)), la.ctypes.data, da.ctypes.data,
+                                           r.ctypes.data, r.size, dk.ctypes.data, dv.ctypes.data,
+                                           self._threads(nthreads))
+        self._check(rc, "oracle_attn_bwd_keys")
+        return dk, dv
+
+    def attn_bwd(self, q, k, v, dout, scale: float, causal: bool, nthreads=None):
+        """dq ``[B,Hq,S,D]``, dk and dv ``[B,Hkv,S,D]`` for output gradient dout."""
+        B, Hq, S, D = np.shape(q)
+        Hkv = np.shape(k)[1]
+        lse, delta, dq = self.attn_bwd_rows(q, k, v, dout, scale, causal, nthreads=nthreads)
+        dk, dv = self.attn_bwd_keys(q, k, v, dout, scale, causal, lse, delta, nthreads=nthreads)
+        return (dq.reshape(B, Hq, S, D), dk.reshape(B, Hkv, S, D), dv.reshape(B, Hkv, S, D))
 
 
 _DEFAULT = None

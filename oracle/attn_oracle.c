@@ -7,6 +7,8 @@
  * baseline leg use it.  It shares no code with the HIP library.
  *
  * What it computes (sources are the four web pages on attention profiling):
+ *   - The backward pass (gradients of q, k, v), derived from the forward
+ *     definition below by the chain rule; see the backward section.
  *   - The attention formula softmax(Q K^T / sqrt(d_k)) V, as stated in the
  *     "technical deep-dive" of the ainews.cool AttentionProfiler article.
  *   - The five-step causal pipeline of the Hugging Face "Profiling in PyTorch
@@ -399,6 +401,187 @@ int oracle_pv_rows(const float* p, const float* v,
     rc = check_rows(&c.sh, rows, nrows);
     if (rc) return rc;
     return run_rows(pv_row, &c, nrows, 0, nthreads);
+}
+
+/* ------------------------------------------------------------------------ */
+/* backward: gradients of the forward above                                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The forward is out_i = sum_j p_ij v_j with p_ij = exp(s_ij) / sum_j' exp(s_ij')
+ * and s_ij = scale * q_i . k_j over the visible keys.  For a loss with
+ * dL/dout = dout (and no gradient reaching lse), the chain rule gives
+ *   dv_j  = sum_i p_ij dout_i
+ *   dp_ij = dout_i . v_j
+ *   ds_ij = p_ij (dp_ij - delta_i),  delta_i = sum_j p_ij dp_ij
+ *   dq_i  = scale * sum_j ds_ij k_j
+ *   dk_j  = scale * sum_i ds_ij q_i
+ * where the sums over i run over every query (of every query head sharing
+ * key/value head g) that sees key j.  The pages only say that the flash
+ * backward is harder to get right than the forward (ai-manual.ru tutorial,
+ * section 6); the formulas are the derivative of the forward definition.
+ *
+ * Pass 1 (one query row at a time): lse_i, delta_i and dq_i.
+ * Pass 2 (one key row at a time): dk_j and dv_j, recomputing p_ij from the
+ * lse_i and delta_i of pass 1.
+ */
+typedef struct {
+    const float *q, *k, *v, *dout;
+    shape_t sh;
+    double scale;
+    int causal;
+    const int64_t* rows;
+    double *lse, *delta, *dq;          /* pass 1 outputs, one per listed row */
+    const double *lse_all, *delta_all; /* pass 2 inputs, [B, Hq, S]          */
+    double *dk, *dv;                   /* pass 2 outputs, one per listed key */
+} bwd_ctx;
+
+/* scratch: s[S] then dp[S] */
+static void bwd_query_row(void* vctx, int64_t n, double* scratch) {
+    const bwd_ctx* c = (const bwd_ctx*)vctx;
+    const shape_t* sh = &c->sh;
+    int64_t b, h, i;
+    split_row(sh, c->rows[n], &b, &h, &i);
+    const int64_t g = kv_head(sh, h);
+    const int64_t S = sh->S, D = sh->D;
+    const float* qi = c->q + ((b * sh->Hq + h) * S + i) * D;
+    const float* doi = c->dout + ((b * sh->Hq + h) * S + i) * D;
+    const float* kb = c->k + (b * sh->Hkv + g) * S * D;
+    const float* vb = c->v + (b * sh->Hkv + g) * S * D;
+    double* s = scratch;
+    double* dp = scratch + S;
+    double* dq = c->dq + n * D;
+    const int64_t jl = last_key(sh, i, c->causal);
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= jl; ++j) {
+        double dot = 0.0, dpj = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            dot += (double)qi[d] * (double)kb[j * D + d];
+            dpj += (double)doi[d] * (double)vb[j * D + d];
+        }
+        s[j] = c->scale * dot;
+        dp[j] = dpj;
+        if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j <= jl; ++j) l += exp(s[j] - m);
+    const double lse = m + log(l);
+    double delta = 0.0;
+    for (int64_t j = 0; j <= jl; ++j) delta += exp(s[j] - lse) * dp[j];
+    for (int64_t d = 0; d < D; ++d) dq[d] = 0.0;
+    for (int64_t j = 0; j <= jl; ++j) {
+        const double p = exp(s[j] - lse);
+#if ORACLE_PLANT == 8
+        const double ds = p * dp[j]; /* planted: delta left out */
+#else
+        const double ds = p * (dp[j] - delta);
+#endif
+        for (int64_t d = 0; d < D; ++d) {
+#if ORACLE_PLANT == 10
+            dq[d] += ds * (double)vb[j * D + d]; /* planted: v in place of k */
+#else
+            dq[d] += ds * (double)kb[j * D + d];
+#endif
+        }
+    }
+    for (int64_t d = 0; d < D; ++d) dq[d] *= c->scale;
+    c->lse[n] = lse;
+    c->delta[n] = delta;
+}
+
+static void bwd_key_row(void* vctx, int64_t n, double* unused) {
+    (void)unused;
+    const bwd_ctx* c = (const bwd_ctx*)vctx;
+    const shape_t* sh = &c->sh;
+    const int64_t S = sh->S, D = sh->D;
+    const int64_t j = c->rows[n] % S;
+    const int64_t bg = c->rows[n] / S;
+    const int64_t g = bg % sh->Hkv, b = bg / sh->Hkv;
+    const float* kj = c->k + (bg * S + j) * D;
+    const float* vj = c->v + (bg * S + j) * D;
+    double* dk = c->dk + n * D;
+    double* dv = c->dv + n * D;
+    for (int64_t d = 0; d < D; ++d) dk[d] = dv[d] = 0.0;
+    for (int64_t h = 0; h < sh->Hq; ++h) {
+        if (kv_head(sh, h) != g) continue;
+#if ORACLE_PLANT == 12
+        if (h != g * (sh->Hq / sh->Hkv)) continue; /* planted: only the group's first head */
+#endif
+        for (int64_t i = 0; i < S; ++i) {
+#if ORACLE_PLANT == 11
+            if (c->causal && i > j) continue; /* planted: mask direction flipped */
+#else
+            if (last_key(sh, i, c->causal) < j) continue; /* query i does not see key j */
+#endif
+            const int64_t row = (b * sh->Hq + h) * S + i;
+            const float* qi = c->q + row * D;
+            const float* doi = c->dout + row * D;
+            double dot = 0.0, dp = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                dot += (double)qi[d] * (double)kj[d];
+                dp += (double)doi[d] * (double)vj[d];
+            }
+            const double p = exp(c->scale * dot - c->lse_all[row]);
+            const double ds = p * (dp - c->delta_all[row]);
+            for (int64_t d = 0; d < D; ++d) {
+                dv[d] += p * (double)doi[d];
+#if ORACLE_PLANT == 9
+                dk[d] += ds * (double)qi[d]; /* planted: scale dropped */
+#else
+                dk[d] += c->scale * ds * (double)qi[d];
+#endif
+            }
+        }
+    }
+}
+
+/*
+ * Pass 1 for the listed query rows (indices into [B, Hq, S]): lse [nrows],
+ * delta [nrows], dq [nrows, D].  dout has the shape of q.
+ */
+int oracle_attn_bwd_rows(const float* q, const float* k, const float* v, const float* dout,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t S, int64_t D,
+                         double scale, int causal, const int64_t* rows, int64_t nrows,
+                         double* lse, double* delta, double* dq, int nthreads) {
+    bwd_ctx c;
+    memset(&c, 0, sizeof c);
+    c.q = q; c.k = k; c.v = v; c.dout = dout;
+    c.sh.B = B; c.sh.Hq = Hq; c.sh.Hkv = Hkv; c.sh.S = S; c.sh.D = D;
+    c.scale = scale;
+    c.causal = causal ? 1 : 0;
+    c.rows = rows;
+    c.lse = lse; c.delta = delta; c.dq = dq;
+    int rc = check_shape(&c.sh);
+    if (rc) return rc;
+    rc = check_rows(&c.sh, rows, nrows);
+    if (rc) return rc;
+    return run_rows(bwd_query_row, &c, nrows, 2 * S, nthreads);
+}
+
+/*
+ * Pass 2 for the listed key rows (indices into [B, Hkv, S]): dk, dv
+ * [nkeys, D].  lse_all and delta_all are pass 1's results for every query
+ * row, [B, Hq, S].
+ */
+int oracle_attn_bwd_keys(const float* q, const float* k, const float* v, const float* dout,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t S, int64_t D,
+                         double scale, int causal, const double* lse_all, const double* delta_all,
+                         const int64_t* keys, int64_t nkeys, double* dk, double* dv, int nthreads) {
+    bwd_ctx c;
+    memset(&c, 0, sizeof c);
+    c.q = q; c.k = k; c.v = v; c.dout = dout;
+    c.sh.B = B; c.sh.Hq = Hq; c.sh.Hkv = Hkv; c.sh.S = S; c.sh.D = D;
+    c.scale = scale;
+    c.causal = causal ? 1 : 0;
+    c.rows = keys;
+    c.lse_all = lse_all; c.delta_all = delta_all;
+    c.dk = dk; c.dv = dv;
+    int rc = check_shape(&c.sh);
+    if (rc) return rc;
+    const int64_t total = B * Hkv * S;
+    for (int64_t n = 0; n < nkeys; ++n)
+        if (keys[n] < 0 || keys[n] >= total) return -3;
+    return run_rows(bwd_key_row, &c, nkeys, 0, nthreads);
 }
 
 /* Which mistake (0 = none) this build carries; lets a test confirm a variant. */

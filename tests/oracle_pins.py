@@ -21,6 +21,13 @@ What pins what:
     and logsumexp, rows sum to one, zero above the diagonal.
   step 5 (attn v): numpy matmul, exact integer products.
   composition: steps 1-5 chained equal the fused forward.
+  backward (chain-rule derivative of the forward; the ai-manual.ru tutorial,
+  section 6, only warns that the flash backward is easy to get wrong):
+    central finite differences of sum(dout * out) through the pinned forward
+    (GQA, causal and not), torch's float64 autograd through its
+    scaled_dot_product_attention, the invariants sum_j dk_j = 0 and
+    sum_j dv_j = sum_i dout_i, delta_i = dout_i . out_i, S = 1 and causal
+    row 0 closed forms, linearity in dout.
 """
 from __future__ import annotations
 
@@ -393,4 +400,121 @@ def pin_chain_equals_fused(orc):
 STEP_PINS = [pin_qk_numpy, pin_qk_integer, pin_golden_softmax, pin_softmax_scipy,
              pin_pv_numpy, pin_pv_integer, pin_chain_equals_fused]
 
-ALL_PINS = ATTN_PINS + STEP_PINS
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+
+def _dyadic(shape, seed, lo=-2.0, hi=2.0):
+    """Values on a 2^-8 grid: x +- 2^-14 stays exact in float32."""
+    r = _rng(seed)
+    return (np.round(r.uniform(lo, hi, shape) * 256) / 256).astype(np.float32)
+
+
+def pin_bwd_finite_diff(orc):
+    """dq, dk, dv equal central differences of L = sum(dout * out) taken
+    through the (separately pinned) forward, with a step of 2^-14."""
+    h = 2.0 ** -14
+    for (B, Hq, Hkv, S, D, causal, seed) in [(1, 2, 1, 5, 3, True, 60), (1, 2, 1, 5, 3, False, 61),
+                                             (2, 2, 2, 4, 2, True, 62)]:
+        q = _dyadic((B, Hq, S, D), seed)
+        k = _dyadic((B, Hkv, S, D), seed + 10)
+        v = _dyadic((B, Hkv, S, D), seed + 20)
+        do = _dyadic((B, Hq, S, D), seed + 30)
+        sc = 0.75
+
+        def loss(qq, kk, vv):
+            out, _ = orc.attn_fwd(qq, kk, vv, sc, causal)
+            return float(np.sum(out * do.astype(np.float64)))
+
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, sc, causal)
+        for name, x, g in (("dq", q, dq), ("dk", k, dk), ("dv", v, dv)):
+            num = np.zeros(x.shape)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += np.float32(h)
+                xm[idx] -= np.float32(h)
+                args_p = {"dq": (xp, k, v), "dk": (q, xp, v), "dv": (q, k, xp)}[name]
+                args_m = {"dq": (xm, k, v), "dk": (q, xm, v), "dv": (q, k, xm)}[name]
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            _close(g, num, 1e-6, f"finite differences {name} causal={causal}")
+
+
+def pin_bwd_torch(orc):
+    """torch's float64 CPU autograd through scaled_dot_product_attention (an
+    independent library implementation) gives the same dq, dk, dv."""
+    import torch
+
+    for (B, Hq, Hkv, S, D, seed) in [(2, 4, 2, 23, 16, 70), (1, 3, 3, 30, 8, 71), (1, 4, 1, 9, 32, 72)]:
+        q = _randn((B, Hq, S, D), seed)
+        k = _randn((B, Hkv, S, D), seed + 1)
+        v = _randn((B, Hkv, S, D), seed + 2)
+        do = _randn((B, Hq, S, D), seed + 3)
+        sc = 1.0 / math.sqrt(D)
+        g = Hq // Hkv
+        for causal in (True, False):
+            tq = torch.from_numpy(q.astype(np.float64)).requires_grad_()
+            tk = torch.from_numpy(k.astype(np.float64)).requires_grad_()
+            tv = torch.from_numpy(v.astype(np.float64)).requires_grad_()
+            out = torch.nn.functional.scaled_dot_product_attention(
+                tq, tk.repeat_interleave(g, dim=1), tv.repeat_interleave(g, dim=1), is_causal=causal, scale=sc)
+            out.backward(torch.from_numpy(do.astype(np.float64)))
+            dq, dk, dv = orc.attn_bwd(q, k, v, do, sc, causal)
+            _close(dq, tq.grad.numpy(), 1e-11, "torch dq")
+            _close(dk, tk.grad.numpy(), 1e-11, "torch dk")
+            _close(dv, tv.grad.numpy(), 1e-11, "torch dv")
+
+
+def pin_bwd_invariants(orc):
+    """Rows of ds sum to zero, so sum_j dk_j = 0; rows of p sum to one, so
+    sum_j dv_j = sum of dout over the group's queries; delta_i = dout_i . out_i
+    and pass 1's lse equals the forward's."""
+    B, Hq, Hkv, S, D = 2, 6, 2, 37, 8
+    q = _randn((B, Hq, S, D), 80)
+    k = _randn((B, Hkv, S, D), 81)
+    v = _randn((B, Hkv, S, D), 82)
+    do = _randn((B, Hq, S, D), 83)
+    sc = 0.4
+    g = Hq // Hkv
+    for causal in (True, False):
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, sc, causal)
+        _close(dk.sum(axis=2), np.zeros((B, Hkv, D)), 1e-12, "sum dk")
+        ref = do.astype(np.float64).reshape(B, Hkv, g, S, D).sum(axis=(2, 3))
+        _close(dv.sum(axis=2), ref, 1e-11, "sum dv")
+        lse, delta, _ = orc.attn_bwd_rows(q, k, v, do, sc, causal)
+        out, flse = orc.attn_fwd(q, k, v, sc, causal)
+        _close(delta, np.sum(out * do.astype(np.float64), axis=-1).reshape(-1), 1e-12, "delta")
+        _close(lse, flse.reshape(-1), 1e-12, "pass-1 lse")
+
+
+def pin_bwd_special(orc):
+    """S = 1: out = v_0, so dv_0 = sum of dout over the group and dq = dk = 0.
+    Causal query 0 sees one key, so dq_0 = 0; causal key S-1 is seen only by
+    query S-1.  Gradients are linear in dout (doubling is exact)."""
+    q = _randn((1, 4, 1, 5), 90)
+    k = _randn((1, 2, 1, 5), 91)
+    v = _randn((1, 2, 1, 5), 92)
+    do = _randn((1, 4, 1, 5), 93)
+    for causal in (True, False):
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, 0.3, causal)
+        _close(dq, np.zeros_like(dq), 0.0, "S=1 dq")
+        _close(dk, np.zeros_like(dk), 0.0, "S=1 dk")
+        _close(dv, do.astype(np.float64).reshape(1, 2, 2, 1, 5).sum(axis=2), 1e-15, "S=1 dv")
+    B, Hq, S, D = 1, 1, 12, 6
+    q = _randn((B, Hq, S, D), 94)
+    k = _randn((B, Hq, S, D), 95)
+    v = _randn((B, Hq, S, D), 96)
+    do = _randn((B, Hq, S, D), 97)
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, 0.5, True)
+    _close(dq[0, 0, 0], np.zeros(D), 0.0, "causal dq_0")
+    _, lse = orc.attn_fwd(q, k, v, 0.5, True)
+    p_last = math.exp(0.5 * float(np.dot(q[0, 0, -1].astype(np.float64), k[0, 0, -1])) - lse[0, 0, -1])
+    _close(dv[0, 0, -1], p_last * do[0, 0, -1].astype(np.float64), 1e-14, "causal dv_last")
+    dq2, dk2, dv2 = orc.attn_bwd(q, k, v, 2 * do, 0.5, True)
+    _close(dq2, 2 * dq, 0.0, "linear dq")
+    _close(dk2, 2 * dk, 0.0, "linear dk")
+    _close(dv2, 2 * dv, 0.0, "linear dv")
+
+
+BWD_PINS = [pin_bwd_finite_diff, pin_bwd_torch, pin_bwd_invariants, pin_bwd_special]
+
+ALL_PINS = ATTN_PINS + STEP_PINS + BWD_PINS

@@ -22,6 +22,11 @@ PLANTS = {
     5: "GQA heads grouped by stride",
     6: "normalisation dropped",
     7: "lse in base 2",
+    8: "backward delta left out",
+    9: "backward dk scale dropped",
+    10: "backward dq uses v for k",
+    11: "backward key pass mask flipped",
+    12: "backward dk dv from one head of the group",
 }
 
 
@@ -67,3 +72,21 @@ def test_bad_rows_rejected(orc):
         orc.attn_fwd(q, q, q, 1.0, True, rows=np.array([4], np.int64))
     with pytest.raises(RuntimeError):
         orc.attn_fwd(q, q, q, 1.0, True, rows=np.array([-1], np.int64))
+
+
+def test_bwd_rows_keys_match_full(orc):
+    """Sampled query rows and key rows of the backward equal the full result."""
+    rng = np.random.default_rng(51)
+    q = rng.standard_normal((2, 4, 20, 8)).astype(np.float32)
+    k = rng.standard_normal((2, 2, 20, 8)).astype(np.float32)
+    v = rng.standard_normal((2, 2, 20, 8)).astype(np.float32)
+    do = rng.standard_normal((2, 4, 20, 8)).astype(np.float32)
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, 0.3, True)
+    rows = np.array([0, 19, 20, 77, 159], np.int64)
+    lse, delta, dq2 = orc.attn_bwd_rows(q, k, v, do, 0.3, True, rows=rows)
+    assert np.array_equal(dq2, dq.reshape(-1, 8)[rows])
+    la, da, _ = orc.attn_bwd_rows(q, k, v, do, 0.3, True)
+    keys = np.array([0, 7, 39, 79], np.int64)
+    dk2, dv2 = orc.attn_bwd_keys(q, k, v, do, 0.3, True, la, da, keys=keys)
+    assert np.array_equal(dk2, dk.reshape(-1, 8)[keys])
+    assert np.array_equal(dv2, dv.reshape(-1, 8)[keys])
