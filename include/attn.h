@@ -19,6 +19,7 @@
  *   - the unfused trio attn_qk_gemm_* -> attn_masked_softmax_* ->
  *     attn_pv_gemm_*, three kernels that materialise scores and
  *     probabilities in caller-owned buffers, mirroring the naive pipeline.
+ * and, for training, attn_bwd_bf16: the gradients of the fused forward.
  *
  * Conventions shared by every call
  *   Layout     q and out are [B, Hq, S, D]; k and v are [B, Hkv, S, D];
@@ -122,6 +123,34 @@ attn_status attn_pv_gemm_bf16(const void* p, const void* v, void* out,
                               int B, int Hq, int Hkv, int S, int D, void* stream);
 attn_status attn_pv_gemm_f32(const float* p, const float* v, float* out,
                              int B, int Hq, int Hkv, int S, int D, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward of the fused forward (bfloat16).
+ *
+ * Given dout = dL/dout for the forward above (no gradient reaches lse):
+ *   delta_i = dout_i . out_i,  dp_ij = dout_i . v_j,
+ *   ds_ij = p_ij (dp_ij - delta_i),  p_ij = exp(scale q_i . k_j - lse_i),
+ *   dq_i = scale sum_j ds_ij k_j,   dk_j = scale sum_i ds_ij q_i,
+ *   dv_j = sum_i p_ij dout_i,
+ * the sums over i running over every query that sees key j, in every query
+ * head of the key/value head's group.  This is the chain-rule derivative of
+ * the forward; the pages only warn that the flash backward is the delicate
+ * part (ai-manual.ru tutorial, section 6).
+ *
+ * q, k, v, causal, scale: as passed to attn_fwd_bf16.  out, lse: that call's
+ * results (lse is required here).  dout: bfloat16 [B,Hq,S,D].
+ * dq [B,Hq,S,D], dk and dv [B,Hkv,S,D]: bfloat16 outputs, fully written.
+ * delta: float32 workspace of attn_bwd_workspace_bytes(B, Hq, S) bytes,
+ * overwritten (it ends up holding delta_i).  Outputs and workspace must not
+ * overlap the inputs or each other.  Three kernel launches on stream; the
+ * probabilities are recomputed on chip, so no S x S buffer is involved.
+ * ------------------------------------------------------------------------- */
+attn_status attn_bwd_bf16(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, float* delta,
+                          int B, int Hq, int Hkv, int S, int D, float scale, int causal,
+                          void* stream);
+/* Bytes of attn_bwd_bf16's delta workspace: B*Hq*S*4, or 0 on a bad size. */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int S);
 
 /* Bytes of the float32 score buffer: B*Hq*S*S*4, or 0 if a size is < 1 or
  * the product overflows size_t. */

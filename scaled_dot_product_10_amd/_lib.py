@@ -38,6 +38,8 @@ SIGNATURES = {
     "attn_masked_softmax_f32": (_i, [_p, _p, _p, _i, _i, _i, _f, _i, _p]),
     "attn_pv_gemm_bf16": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "attn_pv_gemm_f32": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p]),
+    "attn_bwd_bf16": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
+    "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i]),
     "attn_scores_bytes": (ctypes.c_size_t, [_i, _i, _i]),
     "attn_probs_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "attn_status_str": (ctypes.c_char_p, [_i]),
@@ -107,6 +109,15 @@ def attn_pv_gemm_bf16(p, v, out, B, Hq, Hkv, S, D, stream) -> int:
 
 def attn_pv_gemm_f32(p, v, out, B, Hq, Hkv, S, D, stream) -> int:
     return _call("attn_pv_gemm_f32", p, v, out, B, Hq, Hkv, S, D, stream)
+
+
+def attn_bwd_bf16(q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, S, D, scale, causal, stream) -> int:
+    return _call("attn_bwd_bf16", q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, S, D, scale, causal,
+                 stream)
+
+
+def attn_bwd_workspace_bytes(B, Hq, S) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, Hq, S))
 
 
 def attn_scores_bytes(B, Hq, S) -> int:

@@ -140,3 +140,36 @@ def unfused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool =
     p, lse = masked_softmax(scores, scale=scale, causal=causal, dtype=q.dtype)
     del scores
     return pv_gemm(p, v), lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, *, causal: bool = True, scale: float | None = None, delta: torch.Tensor | None = None):
+    """Gradients of the fused forward (bf16).  ``out``, ``lse``: the forward's
+    results for the same q, k, v, causal and scale; ``dout``: dL/dout.
+
+    Returns ``(dq, dk, dv)``, bf16, shaped like q, k, v.  ``delta`` (float32
+    ``[B,Hq,S]``, optional) is the workspace; it is allocated when absent.
+    """
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check(t, n, torch.bfloat16)
+    _check(lse, "lse", torch.float32, 3)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, S, D) or tuple(v.shape) != (B, Hkv, S, D):
+        raise ValueError(f"k/v shapes {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, S):
+        raise ValueError("out/dout must be shaped like q and lse [B,Hq,S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if delta is None:
+        delta = torch.empty((B, Hq, S), device=q.device, dtype=torch.float32)
+    else:
+        _check(delta, "delta", torch.float32, 3)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    code = _lib.attn_bwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                              lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                              B, Hq, Hkv, S, D, float(scale), int(bool(causal)), _stream(q.device))
+    _raise(code, "attn_bwd_bf16")
+    return dq, dk, dv

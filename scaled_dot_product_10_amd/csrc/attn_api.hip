@@ -1,5 +1,5 @@
 // C ABI of libattn (declared in include/attn.h): argument checks, then one
-// kernel launch per call.  Checks run before any HIP call, so a rejected call
+// kernel launch per call (three for the backward).  Checks run before any HIP call, so a rejected call
 // has no side effect at all.
 #include <math.h>
 #include <stdint.h>
@@ -112,6 +112,38 @@ attn_status check_pv(const void* p, const void* v, const void* out, int B, int H
     if (prod({B, Hq, (S + 63) / 64, 2}) > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
     if (misaligned(p, 16) || misaligned(v, 16) || misaligned(out, 16)) return ATTN_ERR_MISALIGNED;
     if (overlap(out, no, p, np) || overlap(out, no, v, nv)) return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+attn_status check_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, const void* dq, const void* dk, const void* dv, const float* delta, int B,
+                      int Hq, int Hkv, int S, int D, float scale, int causal) {
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL_POINTER;
+    if (bad_dims(B, Hq, Hkv, S)) return ATTN_ERR_BAD_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_BAD_SCALE;
+    const int64_t nq = prod({B, Hq, S, D, 2});
+    const int64_t nkv = prod({B, Hkv, S, D, 2});
+    const int64_t nl = prod({B, Hq, S, 4});
+    if (nq < 0 || nkv < 0 || nl < 0) return ATTN_ERR_BAD_SHAPE;
+    if (prod({B, Hq, (S + 15) / 16}) > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
+        misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) ||
+        misaligned(lse, 4) || misaligned(delta, 4))
+        return ATTN_ERR_MISALIGNED;
+    struct Range {
+        const void* p;
+        int64_t n;
+    };
+    const Range ins[] = {{q, nq}, {k, nkv}, {v, nkv}, {out, nq}, {dout, nq}, {lse, nl}};
+    const Range outs[] = {{dq, nq}, {dk, nkv}, {dv, nkv}, {delta, nl}};
+    for (const Range& o : outs) {
+        for (const Range& i : ins)
+            if (overlap(o.p, o.n, i.p, i.n)) return ATTN_ERR_ALIAS;
+        for (const Range& o2 : outs)
+            if (&o2 != &o && overlap(o.p, o.n, o2.p, o2.n)) return ATTN_ERR_ALIAS;
+    }
     return ATTN_OK;
 }
 
@@ -232,6 +264,37 @@ attn_status attn_pv_gemm_bf16(const void* p, const void* v, void* out, int B, in
 attn_status attn_pv_gemm_f32(const float* p, const float* v, float* out, int B, int Hq, int Hkv, int S, int D,
                              void* stream) {
     return pv_common(p, v, out, B, Hq, Hkv, S, D, stream, 4);
+}
+
+attn_status attn_bwd_bf16(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv,
+                          int S, int D, float scale, int causal, void* stream) {
+    const attn_status st = check_bwd(q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, S, D, scale, causal);
+    if (st != ATTN_OK) return st;
+    attn::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.dout = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = delta;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.S = S;
+    a.D = D;
+    a.scale = scale;
+    a.causal = causal;
+    return hip_status(attn::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int S) {
+    const int64_t n = prod({B, Hq, S, 4});
+    return n < 0 ? 0 : (size_t)n;
 }
 
 size_t attn_scores_bytes(int B, int Hq, int S) {

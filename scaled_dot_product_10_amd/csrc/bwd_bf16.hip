@@ -1,0 +1,471 @@
+// Attention backward, bfloat16 in and out, float32 accumulation.
+//
+// The gradients are the chain-rule derivative of the forward
+// out_i = sum_j p_ij v_j, p_ij = exp(s_ij - lse_i), s_ij = scale q_i . k_j
+// (the forward formula of the ainews.cool deep-dive, causal mask as in the
+// Hugging Face article's "Naive Attention" section; the ai-manual.ru
+// tutorial, section 6, warns that the flash backward is the delicate part):
+//
+//   delta_i = dout_i . out_i                     (= sum_j p_ij dp_ij)
+//   dp_ij   = dout_i . v_j
+//   ds_ij   = p_ij (dp_ij - delta_i)
+//   dv_j    = sum_i p_ij dout_i
+//   dk_j    = scale sum_i ds_ij q_i
+//   dq_i    = scale sum_j ds_ij k_j
+//
+// Three kernels, none of which writes an S x S matrix: p is recomputed on
+// chip from the forward's lse in both main kernels.
+//   bwd_delta_kernel   delta_i, one pass over out and dout.
+//   bwd_dkdv_kernel    a workgroup owns 128 keys of one key/value head and
+//                      sweeps every query (of every query head of its group)
+//                      that sees them: S = Q K^T and dP = dO V^T with K, V in
+//                      registers, then dV^T += dO^T P and dK^T += Q^T dS with
+//                      Q and dO read transposed from LDS.
+//   bwd_dq_kernel      a workgroup owns 128 queries and sweeps their keys:
+//                      S^T = K Q^T and dP^T = V dO^T with Q, dO in
+//                      registers, then dQ^T += K^T dS^T with K read
+//                      transposed from LDS.
+// dq is computed by its own kernel rather than by atomic adds from the dK/dV
+// sweep: two more products per tile, but no read-modify-write traffic and a
+// deterministic result.
+//
+// MFMA layouts are those of v_mfma_f32_32x32x16_bf16 (common.h).  In both
+// main kernels the probabilities and ds come out of an accumulator whose
+// lane owns one column; a 16-row block of it is exactly the B operand of the
+// next product when the A operand's k order is the accumulator's row order
+// (rows 4g..4g+3 and 8+4g..8+4g+3 for lane half g), which the transposed
+// LDS read provides.
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int NT = 256;       // 4 waves
+constexpr int KEYS_WG = 128;  // keys per dK/dV workgroup (32 per wave)
+constexpr int QRY_TILE = 64;  // queries per step of the dK/dV sweep
+constexpr int QRY_WG = 128;   // queries per dQ workgroup (32 per wave)
+constexpr int KEY_TILE = 64;  // keys per step of the dQ sweep
+
+struct BwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* out;
+    const uint16_t* dout;
+    const float* lse;
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    float* delta;
+    int B, Hq, Hkv, S, group;
+    int ntiles;      // workgroups per head (key tiles or query tiles)
+    uint32_t total;  // workgroups in the grid
+    float c;         // scale * log2(e)
+    float scale;
+    int causal;
+};
+
+// LDS tile of rows x D bf16 (row-major, 16-byte chunks), read two ways: a
+// row read (16 bytes of one row per lane: 16 lanes on 16 consecutive rows)
+// and a transposed read (ds_read_b64_tr_b16: 16 lanes on 4 consecutive rows,
+// 32 bytes of each).  Chunk c of row r sits at chunk position c ^ swz(r),
+// which keeps both patterns free of bank conflicts.
+template <int D>
+struct SwzTile {
+    static constexpr int CPR = D / 8;
+    __device__ static int swz(int r) {
+        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    }
+    // element offset of 8-aligned column col of row r
+    __device__ static int at(int r, int col) { return r * D + ((((col >> 3) ^ swz(r))) << 3) + (col & 7); }
+};
+
+// Rows [r0, r0 + ROWS) of a [S, D] bf16 matrix -> registers, 16 bytes per
+// thread per instruction, D/8 lanes per row (whole cache lines); rows past S
+// are zero.  store() writes them to a SwzTile.
+template <int D, int ROWS>
+struct RowTile {
+    static constexpr int CPR = D / 8;
+    static constexpr int CH = ROWS * CPR / NT;
+    static_assert(CH * NT == ROWS * CPR, "tile/thread mismatch");
+    u32x4 r[CH];
+    __device__ __forceinline__ void load(const uint16_t* base, int r0, int S, int tid) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = tid + NT * i, row = r0 + c / CPR;
+            r[i] = row < S ? *(const u32x4*)(base + (int64_t)row * D + (c % CPR) * 8) : u32x4{0, 0, 0, 0};
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* t, int tid) const {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = tid + NT * i;
+            *(u32x4*)(t + SwzTile<D>::at(c / CPR, (c % CPR) * 8)) = r[i];
+        }
+    }
+};
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int half) {
+    const u32x4 w = {pack_bf16x2(x[8 * half + 0], x[8 * half + 1]), pack_bf16x2(x[8 * half + 2], x[8 * half + 3]),
+                     pack_bf16x2(x[8 * half + 4], x[8 * half + 5]), pack_bf16x2(x[8 * half + 6], x[8 * half + 7])};
+    return as_bf16x8(w);
+}
+
+// Per-lane offsets of the transposed read of a 16-row block (rows 16kb + ..)
+// of a SwzTile: lane j of 16-lane group G reads row 4(G/2) + j/4 (k-slots
+// 0-3) and that row + 8 (k-slots 4-7), columns 32db + 16(G%2) + 4(j%4) .. +3.
+// Adding 16 rows leaves the swizzle unchanged, so block kb is + 16 kb D.
+template <int D>
+struct TrOffsets {
+    static constexpr int DB = D / 32;
+    int lo[DB], hi[DB];
+    __device__ __forceinline__ void init(int lane) {
+        const int G = lane >> 4, j = lane & 15;
+        const int r = 4 * (G >> 1) + (j >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + (G & 1) * 16 + 4 * (j & 3);
+            lo[db] = SwzTile<D>::at(r, col);
+            hi[db] = SwzTile<D>::at(r + 8, col);
+        }
+    }
+    __device__ __forceinline__ bf16x8 read(const uint16_t* t, int kb, int db) const {
+        return tr_read_pair(t + kb * 16 * D + lo[db], t + kb * 16 * D + hi[db]);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// delta_i = sum_d dout[i][d] out[i][d]; D/8 lanes per row, 16 bytes each.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(NT) void bwd_delta_kernel(BwdParams p, int64_t rows) {
+    constexpr int LPR = D / 8;         // lanes per row
+    constexpr int RPB = NT / LPR;      // rows per block
+    const int tid = threadIdx.x;
+    const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
+    const int col = (tid % LPR) * 8;
+    float acc = 0.f;
+    if (row < rows) {
+        const u32x4 a = *(const u32x4*)(p.out + row * D + col);
+        const u32x4 b = *(const u32x4*)(p.dout + row * D + col);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a0 = __uint_as_float(a[e] << 16), a1 = __uint_as_float(a[e] & 0xffff0000u);
+            const float b0 = __uint_as_float(b[e] << 16), b1 = __uint_as_float(b[e] & 0xffff0000u);
+            acc = fmaf(a0, b0, fmaf(a1, b1, acc));
+        }
+    }
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (row < rows && tid % LPR == 0) p.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  Workgroup = (b, kv head g, 128-key tile); wave w owns keys
+// n0 + 32w .. +31 (lane l32 = key).  Sweeps the query heads of the group and
+// their 64-query tiles from the first one that sees the keys.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdParams p) {
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    using TQ = RowTile<D, QRY_TILE>;
+    __shared__ __attribute__((aligned(16))) uint16_t Qs[QRY_TILE * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Os[QRY_TILE * D];  // dout tile
+    __shared__ __attribute__((aligned(16))) float Ls[QRY_TILE];        // lse * log2(e); +inf past S
+    __shared__ __attribute__((aligned(16))) float Ds[QRY_TILE];        // delta
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+    const uint32_t L = xcd_remap(blockIdx.x, p.total);
+    const int bg = (int)(L / (uint32_t)p.ntiles);
+    const int tile = (int)(L % (uint32_t)p.ntiles);  // ascending: longest sweeps first under the mask
+    const int b = bg / p.Hkv, kvh = bg % p.Hkv;
+    const int S = p.S;
+    const int n0 = tile * KEYS_WG;
+    const int key = n0 + wave * 32 + l32;
+    const uint16_t* kb = p.k + (int64_t)bg * S * D;
+    const uint16_t* vb = p.v + (int64_t)bg * S * D;
+
+    bf16x8 kreg[KS], vreg[KS];  // B operands: column = this lane's key, k = d
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
+        if (key < S) {
+            a = *(const u32x4*)(kb + (int64_t)key * D + ks * 16 + g * 8);
+            c = *(const u32x4*)(vb + (int64_t)key * D + ks * 16 + g * 8);
+        }
+        kreg[ks] = as_bf16x8(a);
+        vreg[ks] = as_bf16x8(c);
+    }
+    int roff[KS];  // row read of row l32, chunk 2ks + g
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) roff[ks] = SwzTile<D>::at(l32, (2 * ks + g) * 8);
+    TrOffsets<D> tr;
+    tr.init(lane);
+
+    f32x16 dvacc[DB], dkacc[DB];  // dV^T, dK^T: rows d, column = key
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dvacc[db] = dkacc[db] = f32x16{};
+
+    const int nqt = (S + QRY_TILE - 1) / QRY_TILE;
+    const int qt0 = CAUSAL ? n0 / QRY_TILE : 0;
+    const int steps = (nqt - qt0) * p.group;  // (head, query tile) pairs
+    const float c = p.c;
+    const float kLog2eF = kLog2e;
+
+    TQ tq, to;
+    float lnext = 0.f, dnext = 0.f;
+    auto fetch = [&](int s) __attribute__((always_inline)) {
+        const int h = kvh * p.group + s / (nqt - qt0);
+        const int m0 = (qt0 + s % (nqt - qt0)) * QRY_TILE;
+        const int64_t rowb = ((int64_t)b * p.Hq + h) * S;
+        tq.load(p.q + rowb * D, m0, S, tid);
+        to.load(p.dout + rowb * D, m0, S, tid);
+        if (tid < QRY_TILE) {
+            const int i = m0 + tid;
+            lnext = i < S ? p.lse[rowb + i] * kLog2eF : INFINITY;
+            dnext = i < S ? p.delta[rowb + i] : 0.f;
+        }
+    };
+    if (steps > 0) fetch(0);
+    for (int s = 0; s < steps; ++s) {
+        const int m0 = (qt0 + s % (nqt - qt0)) * QRY_TILE;
+        __syncthreads();  // previous tile consumed
+        tq.store(Qs, tid);
+        to.store(Os, tid);
+        if (tid < QRY_TILE) {
+            Ls[tid] = lnext;
+            Ds[tid] = dnext;
+        }
+        __syncthreads();
+        if (s + 1 < steps) fetch(s + 1);
+#pragma unroll
+        for (int xb = 0; xb < 2; ++xb) {
+            const int qb = m0 + xb * 32;  // first query of this 32-query block
+            // every query of the block is before every key of the wave: nothing visible
+            if (CAUSAL && qb + 31 < n0 + wave * 32) continue;
+            f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 aq = *(const bf16x8*)(Qs + xb * 32 * D + roff[ks]);
+                const bf16x8 ao = *(const bf16x8*)(Os + xb * 32 * D + roff[ks]);
+                sacc = mfma32x32x16(aq, kreg[ks], sacc);
+                dpacc = mfma32x32x16(ao, vreg[ks], dpacc);
+            }
+            // row r of the accumulators: query qb + 8(r/4) + 4g + r%4
+            f32x16 pv, dsv;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int rl = xb * 32 + q4 * 8 + g * 4;
+                const f32x4 l4 = *(const f32x4*)(Ls + rl);
+                const f32x4 d4 = *(const f32x4*)(Ds + rl);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = q4 * 4 + e;
+                    float pr = fast_exp2(fmaf(sacc[r], c, -l4[e]));
+                    if (CAUSAL && key > m0 + rl + e) pr = 0.f;
+                    pv[r] = pr;
+                    dsv[r] = pr * (dpacc[r] - d4[e]);
+                }
+            }
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const bf16x8 pb = pack8(pv, half);
+                const bf16x8 db8 = pack8(dsv, half);
+                const int kblk = xb * 2 + half;  // 16-query block of the tile
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dvacc[db] = mfma32x32x16(tr.read(Os, kblk, db), pb, dvacc[db]);
+                    dkacc[db] = mfma32x32x16(tr.read(Qs, kblk, db), db8, dkacc[db]);
+                }
+            }
+        }
+    }
+    if (key < S) {
+        uint16_t* dkr = p.dk + ((int64_t)bg * S + key) * D;
+        uint16_t* dvr = p.dv + ((int64_t)bg * S + key) * D;
+        const float sc = p.scale;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = db * 32 + j * 8 + g * 4;
+                *(u32x2*)(dkr + d0) = u32x2{pack_bf16x2(dkacc[db][4 * j] * sc, dkacc[db][4 * j + 1] * sc),
+                                            pack_bf16x2(dkacc[db][4 * j + 2] * sc, dkacc[db][4 * j + 3] * sc)};
+                *(u32x2*)(dvr + d0) = u32x2{pack_bf16x2(dvacc[db][4 * j], dvacc[db][4 * j + 1]),
+                                            pack_bf16x2(dvacc[db][4 * j + 2], dvacc[db][4 * j + 3])};
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  Workgroup = (b, h, 128-query tile), longest (last) tiles first; wave w
+// owns queries m0 + 32w .. +31 (lane l32 = query).  Sweeps 64-key tiles.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdParams p) {
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    using TK = RowTile<D, KEY_TILE>;
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[KEY_TILE * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[KEY_TILE * D];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+    const uint32_t L = xcd_remap(blockIdx.x, p.total);
+    const int bh = (int)(L / (uint32_t)p.ntiles);
+    const int tile = p.ntiles - 1 - (int)(L % (uint32_t)p.ntiles);
+    const int b = bh / p.Hq, h = bh % p.Hq, kvh = h / p.group;
+    const int S = p.S;
+    const int m0 = tile * QRY_WG;
+    const int qw = m0 + wave * 32;  // first query of this wave
+    const int qi = qw + l32;
+    const int64_t rowb = (int64_t)bh * S;
+    const uint16_t* kb = p.k + ((int64_t)b * p.Hkv + kvh) * S * D;
+    const uint16_t* vb = p.v + ((int64_t)b * p.Hkv + kvh) * S * D;
+
+    bf16x8 qreg[KS], oreg[KS];  // B operands: column = this lane's query, k = d
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
+        if (qi < S) {
+            a = *(const u32x4*)(p.q + (rowb + qi) * D + ks * 16 + g * 8);
+            c = *(const u32x4*)(p.dout + (rowb + qi) * D + ks * 16 + g * 8);
+        }
+        qreg[ks] = as_bf16x8(a);
+        oreg[ks] = as_bf16x8(c);
+    }
+    const float l2 = qi < S ? p.lse[rowb + qi] * kLog2e : INFINITY;
+    const float dl = qi < S ? p.delta[rowb + qi] : 0.f;
+    int roff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) roff[ks] = SwzTile<D>::at(l32, (2 * ks + g) * 8);
+    TrOffsets<D> tr;
+    tr.init(lane);
+
+    f32x16 dqacc[DB];  // dQ^T: rows d, column = query
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
+
+    const int qlast = min(m0 + QRY_WG, S) - 1;
+    const int nkt = CAUSAL ? qlast / KEY_TILE + 1 : (S + KEY_TILE - 1) / KEY_TILE;
+    const float c = p.c;
+    TK tk, tv;
+    tk.load(kb, 0, S, tid);
+    tv.load(vb, 0, S, tid);
+    for (int t = 0; t < nkt; ++t) {
+        const int k0 = t * KEY_TILE;
+        __syncthreads();
+        tk.store(Ks, tid);
+        tv.store(Vs, tid);
+        __syncthreads();
+        if (t + 1 < nkt) {
+            tk.load(kb, k0 + KEY_TILE, S, tid);
+            tv.load(vb, k0 + KEY_TILE, S, tid);
+        }
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int kb0 = k0 + sb * 32;
+            if (CAUSAL && kb0 > qw + 31) continue;  // every key after every query of the wave
+            f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 ak = *(const bf16x8*)(Ks + sb * 32 * D + roff[ks]);
+                const bf16x8 av = *(const bf16x8*)(Vs + sb * 32 * D + roff[ks]);
+                sacc = mfma32x32x16(ak, qreg[ks], sacc);
+                dpacc = mfma32x32x16(av, oreg[ks], dpacc);
+            }
+            // row r: key kb0 + 8(r/4) + 4g + r%4
+            f32x16 dsv;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kj = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                float pr = fast_exp2(fmaf(sacc[r], c, -l2));
+                if (kj >= S || (CAUSAL && kj > qi)) pr = 0.f;
+                dsv[r] = pr * (dpacc[r] - dl);
+            }
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const bf16x8 db8 = pack8(dsv, half);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) dqacc[db] = mfma32x32x16(tr.read(Ks, sb * 2 + half, db), db8, dqacc[db]);
+            }
+        }
+    }
+    if (qi < S) {
+        uint16_t* r = p.dq + (rowb + qi) * D;
+        const float sc = p.scale;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = db * 32 + j * 8 + g * 4;
+                *(u32x2*)(r + d0) = u32x2{pack_bf16x2(dqacc[db][4 * j] * sc, dqacc[db][4 * j + 1] * sc),
+                                          pack_bf16x2(dqacc[db][4 * j + 2] * sc, dqacc[db][4 * j + 3] * sc)};
+            }
+        }
+    }
+}
+
+template <typename K>
+hipError_t launch(K kernel, uint32_t grid, const BwdParams& prm, hipStream_t stream) {
+    BwdParams arg = prm;
+    void* args[] = {&arg};
+    return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(NT), args, 0, stream);
+}
+
+template <typename K>
+hipError_t launch_delta(K kernel, int64_t rows, int rpb, const BwdParams& prm, hipStream_t stream) {
+    BwdParams arg = prm;
+    int64_t n = rows;
+    void* args[] = {&arg, &n};
+    return hipLaunchKernel((const void*)kernel, dim3((uint32_t)((rows + rpb - 1) / rpb)), dim3(NT), args, 0, stream);
+}
+
+template <int D>
+hipError_t run(BwdParams prm, const BwdArgs& a, hipStream_t stream) {
+    const int64_t rows = (int64_t)a.B * a.Hq * a.S;
+    hipError_t e = launch_delta(&bwd_delta_kernel<D>, rows, NT / (D / 8), prm, stream);
+    if (e != hipSuccess) return e;
+    prm.ntiles = (a.S + KEYS_WG - 1) / KEYS_WG;
+    prm.total = (uint32_t)((int64_t)a.B * a.Hkv * prm.ntiles);
+    e = a.causal ? launch(&bwd_dkdv_kernel<D, true>, prm.total, prm, stream)
+                 : launch(&bwd_dkdv_kernel<D, false>, prm.total, prm, stream);
+    if (e != hipSuccess) return e;
+    prm.ntiles = (a.S + QRY_WG - 1) / QRY_WG;
+    prm.total = (uint32_t)((int64_t)a.B * a.Hq * prm.ntiles);
+    return a.causal ? launch(&bwd_dq_kernel<D, true>, prm.total, prm, stream)
+                    : launch(&bwd_dq_kernel<D, false>, prm.total, prm, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+    BwdParams prm;
+    prm.q = (const uint16_t*)a.q;
+    prm.k = (const uint16_t*)a.k;
+    prm.v = (const uint16_t*)a.v;
+    prm.out = (const uint16_t*)a.out;
+    prm.dout = (const uint16_t*)a.dout;
+    prm.lse = a.lse;
+    prm.dq = (uint16_t*)a.dq;
+    prm.dk = (uint16_t*)a.dk;
+    prm.dv = (uint16_t*)a.dv;
+    prm.delta = a.delta;
+    prm.B = a.B;
+    prm.Hq = a.Hq;
+    prm.Hkv = a.Hkv;
+    prm.S = a.S;
+    prm.group = a.Hq / a.Hkv;
+    prm.ntiles = 0;
+    prm.total = 0;
+    prm.c = a.scale * kLog2e;
+    prm.scale = a.scale;
+    prm.causal = a.causal;
+    return a.D == 128 ? run<128>(prm, a, stream) : run<64>(prm, a, stream);
+}
+
+}  // namespace attn

@@ -1,5 +1,6 @@
 // Internal launchers behind the C ABI (include/attn.h).  Arguments are
-// already validated by the caller; each launcher enqueues exactly one kernel.
+// already validated by the caller; each launcher enqueues exactly one kernel,
+// except the backward's, which enqueues three.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,6 +41,22 @@ struct PvArgs {
     int B, Hq, Hkv, S, D;
 };
 
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;  // workspace [B, Hq, S]
+    int B, Hq, Hkv, S, D;
+    float scale;
+    int causal;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_qk_gemm_bf16(const QkArgs& a, hipStream_t stream);
@@ -48,5 +65,6 @@ hipError_t launch_masked_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream);
 hipError_t launch_masked_softmax_f32(const SoftmaxArgs& a, hipStream_t stream);
 hipError_t launch_pv_gemm_bf16(const PvArgs& a, hipStream_t stream);
 hipError_t launch_pv_gemm_f32(const PvArgs& a, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);  // three kernels
 
 }  // namespace attn

@@ -68,6 +68,14 @@ def make_qkv(B: int, Hq: int, Hkv: int, S: int, D: int, dtype: str, seed: int):
     return _finish(q, dtype), _finish(k, dtype), _finish(v, dtype)
 
 
+def make_dout(B: int, Hq: int, S: int, D: int, dtype: str, seed: int) -> Tensor:
+    """Output gradient ``[B,Hq,S,D]`` for the backward, iid N(0,1), drawn from
+    a stream of its own (PCG64 seeded with ``[seed, 1]``), so q, k, v of the
+    same seed are unchanged."""
+    rng = np.random.default_rng([seed, 1])
+    return _finish(rng.standard_normal((B, Hq, S, D), dtype=np.float32), dtype)
+
+
 def make_scores(B: int, H: int, S: int, D: int, seed: int) -> np.ndarray:
     """Raw (unscaled) score-like matrix ``[B,H,S,S]`` fp32 for the masked softmax alone.
 

@@ -40,7 +40,7 @@ def L():
 
 def test_header_symbols_are_exported(L):
     syms = header_symbols()
-    assert len(syms) == 12, syms
+    assert len(syms) == 14, syms
     nm = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)], capture_output=True, text=True,
                         check=True).stdout
     exported = set(re.findall(r"\bT (\w+)$", nm, flags=re.M))
@@ -73,6 +73,8 @@ def test_byte_helpers(L):
     assert _lib.attn_probs_bytes(1, 1, 8, 3) == 0
     assert _lib.attn_scores_bytes(0, 1, 8) == 0
     assert _lib.attn_scores_bytes(1 << 30, 1 << 30, 1 << 30) == 0
+    assert _lib.attn_bwd_workspace_bytes(4, 16, 4096) == 4 * 16 * 4096 * 4
+    assert _lib.attn_bwd_workspace_bytes(1, 0, 8) == 0
 
 
 FWD = [_lib.attn_fwd_bf16, _lib.attn_fwd_f32]
@@ -132,6 +134,34 @@ def test_pv_rejects():
     assert f(A + 2, Bp, C, 1, 1, 1, 8, 64, None) == ALIGN
     assert f(A, Bp, Bp, 1, 1, 1, 8, 64, None) == ALIAS
     assert _lib.attn_pv_gemm_f32(A, Bp, C, 0, 1, 1, 8, 64, None) == SHAPE
+
+
+F = A + (5 << 36)
+G_ = A + (6 << 36)
+H_ = A + (7 << 36)
+I_ = A + (8 << 36)
+J_ = A + (9 << 36)
+
+
+def bwd_args(**kw):
+    a = dict(q=A, k=Bp, v=C, out=Dp, dout=E, lse=F, dq=G_, dk=H_, dv=I_, delta=J_, B=1, Hq=2, Hkv=1, S=16, D=64,
+             scale=0.125, causal=1, stream=None)
+    a.update(kw)
+    return [a[n] for n in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "delta", "B", "Hq", "Hkv", "S",
+                           "D", "scale", "causal", "stream")]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(out=None), NULL), (dict(dout=None), NULL), (dict(lse=None), NULL),
+    (dict(dq=None), NULL), (dict(dk=None), NULL), (dict(dv=None), NULL), (dict(delta=None), NULL),
+    (dict(B=0), SHAPE), (dict(Hq=3, Hkv=2), SHAPE), (dict(S=0), SHAPE),
+    (dict(D=96), UNSUP), (dict(causal=2), UNSUP), (dict(scale=float("nan")), SCALE), (dict(scale=0.0), SCALE),
+    (dict(dout=E + 8), ALIGN), (dict(dq=G_ + 2), ALIGN), (dict(delta=J_ + 2), ALIGN), (dict(lse=F + 1), ALIGN),
+    (dict(dq=A), ALIAS), (dict(dk=Bp + 32), ALIAS), (dict(dv=E), ALIAS), (dict(delta=F), ALIAS),
+    (dict(dk=G_ + 16), ALIAS), (dict(delta=I_), ALIAS),
+])
+def test_bwd_rejects(kw, code):
+    assert _lib.attn_bwd_bf16(*bwd_args(**kw)) == code
 
 
 def test_missing_library_is_loud(tmp_path, monkeypatch):

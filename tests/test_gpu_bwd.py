@@ -1,0 +1,120 @@
+"""Backward (attn_bwd_bf16) against the fp64 CPU oracle's chain-rule gradients.
+
+The GPU backward runs on the GPU forward's own out and lse, as a training step
+would; the oracle recomputes everything from q, k, v and dout alone.  Small
+shapes are compared over every element of dq, dk and dv; the measured
+workloads on sampled query rows (dq) and on sampled key rows of one key/value
+head (dk, dv), for which the oracle first takes the lse and delta of every
+query row of that head's group.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import gpu_util as G
+from scaled_dot_product_10_amd import api, inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_bwd(q, k, v, do, causal, sc):
+    Q, K, V, DO = G.dev(q), G.dev(k), G.dev(v), G.dev(do)
+    out, lse = api.fwd(Q, K, V, causal=causal, scale=sc)
+    dq, dk, dv = api.bwd(Q, K, V, out, lse, DO, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+SMALL = [
+    (1, 1, 1, 1, 128), (1, 2, 1, 17, 64), (1, 2, 2, 128, 128), (1, 2, 1, 200, 128), (2, 4, 2, 130, 64),
+    (1, 1, 1, 300, 128), (1, 3, 3, 257, 64), (1, 4, 1, 64, 128), (1, 2, 2, 520, 128),
+]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}H{}kv{}S{}D{}".format(*s))
+def test_small_full_compare(orc, shape, causal):
+    B, Hq, Hkv, S, D = shape
+    seed = 2000 + S + D + Hq
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", seed)
+    do = inputs.make_dout(B, Hq, S, D, "bf16", seed)
+    sc = 1.0 / math.sqrt(D)
+    dq, dk, dv = run_bwd(q, k, v, do, causal, sc)
+    rq, rk, rv = orc.attn_bwd(q.f32, k.f32, v.f32, do.f32, sc, causal)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        G.check_grad(f"bwd {shape} causal={causal} {name}", G.host(got), ref)
+
+
+def _sampled(orc, name, causal):
+    c = inputs.CONFIGS[name]
+    B, Hq, Hkv, S, D = c["B"], c["Hq"], c["Hkv"], c["S"], c["D"]
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", c["seed"])
+    do = inputs.make_dout(B, Hq, S, D, "bf16", c["seed"])
+    sc = 1.0 / math.sqrt(D)
+    dq, dk, dv = run_bwd(q, k, v, do, causal, sc)
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    rows = G.sample_rows(B, Hq, S, n_random=200, seed=c["seed"])
+    _, _, rdq = orc.attn_bwd_rows(q.f32, k.f32, v.f32, do.f32, sc, causal, rows=rows)
+    got = dq.view(-1, D)[torch.from_numpy(rows).to(dq.device)]
+    G.check_grad(f"{name} causal={causal} dq rows={rows.size}", G.host(got), rdq)
+    # dk, dv of one key/value head (the last one): the oracle needs lse and
+    # delta of every query row of its group first
+    b, g = B - 1, Hkv - 1
+    grp = Hq // Hkv
+    qrows = np.concatenate([((b * Hq + h) * S + np.arange(S)) for h in range(g * grp, (g + 1) * grp)])
+    lse_all = np.zeros(B * Hq * S)
+    delta_all = np.zeros(B * Hq * S)
+    la, da, _ = orc.attn_bwd_rows(q.f32, k.f32, v.f32, do.f32, sc, causal, rows=qrows)
+    lse_all[qrows] = la
+    delta_all[qrows] = da
+    keys_local = G.sample_rows(1, 1, S, n_random=60, seed=c["seed"] + 1)
+    keys = (b * Hkv + g) * S + keys_local
+    rdk, rdv = orc.attn_bwd_keys(q.f32, k.f32, v.f32, do.f32, sc, causal, lse_all, delta_all, keys=keys)
+    kidx = torch.from_numpy(keys).to(dk.device)
+    G.check_grad(f"{name} causal={causal} dk keys={keys.size}", G.host(dk.view(-1, D)[kidx]), rdk)
+    G.check_grad(f"{name} causal={causal} dv keys={keys.size}", G.host(dv.view(-1, D)[kidx]), rdv)
+
+
+@pytest.mark.parametrize("name,causal", [("C2", True), ("C3", True), ("C3", False), ("C5", True)])
+def test_config_sampled(orc, name, causal):
+    _sampled(orc, name, causal)
+
+
+def test_delta_workspace():
+    """The workspace ends up holding delta_i = dout_i . out_i of the forward's out."""
+    B, Hq, Hkv, S, D = 1, 2, 1, 150, 128
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", 2100)
+    do = inputs.make_dout(B, Hq, S, D, "bf16", 2100)
+    Q, K, V, DO = G.dev(q), G.dev(k), G.dev(v), G.dev(do)
+    out, lse = api.fwd(Q, K, V, causal=True)
+    delta = torch.full((B, Hq, S), float("nan"), device=Q.device)
+    api.bwd(Q, K, V, out, lse, DO, causal=True, delta=delta)
+    torch.cuda.synchronize()
+    ref = (G.host(out) * do.f32.astype(np.float64)).sum(-1)
+    assert np.max(np.abs(G.host(delta) - ref)) <= 1e-5 * max(1.0, np.abs(ref).max())
+
+
+def test_deterministic_and_poisoned():
+    """Two runs agree bit for bit and every output element is written."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 333, 128
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", 2101)
+    do = inputs.make_dout(B, Hq, S, D, "bf16", 2101)
+    Q, K, V, DO = G.dev(q), G.dev(k), G.dev(v), G.dev(do)
+    out, lse = api.fwd(Q, K, V, causal=True)
+    a = api.bwd(Q, K, V, out, lse, DO, causal=True)
+    b = api.bwd(Q, K, V, out, lse, DO, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+        assert bool(torch.isfinite(x.float()).all())
