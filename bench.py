@@ -131,6 +131,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="seconds of untimed steps before the warmup steps (clock ramp-up)")
@@ -262,14 +263,44 @@ def main():
             "ms": {k_: round(v_, 4) for k_, v_ in t_u.items()},
             "total_ms": round(total, 4),
             "fused_speedup": round(total / ms_step, 2),
-            "qk_gemm": {"GB/s": gbs(b_u1, t_u["qk_gemm"]), "bytes": b_u1},
+            "qk_gemm": {"GB/s": gbs(b_u1, t_u["qk_gemm"]), "bytes": b_u1,
+                        "roofline": {"bound": "hbm", "achieved": gbs(b_u1, t_u["qk_gemm"]), "peak": PEAK_HBM_GBS,
+                                     "unit": "GB/s", "frac": round(gbs(b_u1, t_u["qk_gemm"]) / PEAK_HBM_GBS, 4)}},
             "masked_softmax": {"GB/s": gbs(b_u2, t_u["masked_softmax"]), "bytes": b_u2,
                                "roofline": {"bound": "hbm", "achieved": gbs(b_u2, t_u["masked_softmax"]),
                                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                             "frac": round(gbs(b_u2, t_u["masked_softmax"]) / PEAK_HBM_GBS, 4)}},
-            "pv_gemm": {"GB/s": gbs(b_u3, t_u["pv_gemm"]), "bytes": b_u3},
+            "pv_gemm": {"GB/s": gbs(b_u3, t_u["pv_gemm"]), "bytes": b_u3,
+                        "roofline": {"bound": "hbm", "achieved": gbs(b_u3, t_u["pv_gemm"]), "peak": PEAK_HBM_GBS,
+                                     "unit": "GB/s", "frac": round(gbs(b_u3, t_u["pv_gemm"]) / PEAK_HBM_GBS, 4)}},
         }
         del scores, p
+
+    # backward of the same causal step (three launches: delta, dK/dV, dQ);
+    # FLOPs counted as the five products of the gradient formulas
+    bwd = None
+    if not args.no_bwd:
+        do = to_dev(inputs.make_dout(B, Hq, S, D, "bf16", c["seed"]))
+        fused(True)
+        gq, gk, gv = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+        delta = torch.empty((B, Hq, S), device=dev, dtype=torch.float32)
+
+        def backward():
+            rc = _lib.attn_bwd_bf16(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), do.data_ptr(),
+                                    lse.data_ptr(), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(), delta.data_ptr(),
+                                    B, Hq, Hkv, S, D, sc, 1, sp)
+            if rc:
+                raise _lib.AttnError(rc, "attn_bwd_bf16")
+
+        backward()
+        torch.cuda.synchronize()
+        bms = float(np.median(time_launches(backward, 10, stream)))
+        bfl = 2.5 * attn_flops(B, Hq, S, D, True)
+        bwd = {"workload": "causal attention backward B4 H16 S4096 D128 bf16 (dq, dk, dv)",
+               "ms": round(bms, 4), "tflops": round(bfl / (bms * 1e-3) / 1e12, 2),
+               "frac_bf16_peak": round(bfl / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "flops": bfl, "launches": 3}
+        del do, gq, gk, gv, delta
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -297,6 +328,7 @@ def main():
         "cpu_baseline": cpu,
         "noncausal": noncausal,
         "unfused": unfused,
+        "backward": bwd,
         "gpu": props.name,
         "cus": props.multi_processor_count,
         "timed_wall_s": round(wall, 4),
