@@ -13,6 +13,9 @@ profiling; each function's C counterpart states the definition it writes out):
   log-sum-exp: the formula in the ainews.cool "technical deep-dive", with the
   five-step causal pipeline of the Hugging Face article's "Naive Attention"
   section (insight.aitobox.com rendering).
+* ``attn_fwd_local`` -- the same with a causal sliding window (query i sees
+  its own key and the window - 1 before it): one of the special masks that
+  the ai-manual.ru tutorial names as the reason for custom kernels.
 * ``qk_scores``  -- step 1 of that pipeline (q k^T, unscaled).
 * ``masked_softmax`` -- steps 2-4 (scale, mask with -inf, softmax).
 * ``pv``         -- step 5 (attn v).
@@ -70,6 +73,10 @@ class Oracle:
         L.oracle_attn_fwd_rows.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64,
                                            ctypes.c_double, ctypes.c_int, _ptr, _i64, _ptr, _ptr,
                                            ctypes.c_int]
+        L.oracle_attn_fwd_local_rows.restype = ctypes.c_int
+        L.oracle_attn_fwd_local_rows.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64,
+                                                 ctypes.c_double, ctypes.c_int, _i64, _ptr, _i64, _ptr,
+                                                 _ptr, ctypes.c_int]
         L.oracle_qk_scores_rows.restype = ctypes.c_int
         L.oracle_qk_scores_rows.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _ptr, _i64,
                                             _ptr, ctypes.c_int]
@@ -135,6 +142,25 @@ class Oracle:
                                            r.ctypes.data, r.size, out.ctypes.data,
                                            lse.ctypes.data, self._threads(nthreads))
         self._check(rc, "oracle_attn_fwd_rows")
+        if rows is None:
+            return out.reshape(B, Hq, S, D), lse.reshape(B, Hq, S)
+        return out, lse
+
+    def attn_fwd_local(self, q, k, v, scale: float, window: int, rows=None, nthreads=None):
+        """Causal sliding-window attention: query i sees keys
+        max(0, i-window+1)..i.  Same shapes and ``rows`` as ``attn_fwd``."""
+        q, k, v = self._f32(q), self._f32(k), self._f32(v)
+        B, Hq, S, D = q.shape
+        Hkv = k.shape[1]
+        assert k.shape == (B, Hkv, S, D) and v.shape == k.shape and int(window) >= 1
+        r = self._rows(rows, B * Hq * S)
+        out = np.empty((r.size, D), dtype=np.float64)
+        lse = np.empty((r.size,), dtype=np.float64)
+        rc = self.lib.oracle_attn_fwd_local_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                                 B, Hq, Hkv, S, D, float(scale), 1, int(window),
+                                                 r.ctypes.data, r.size, out.ctypes.data,
+                                                 lse.ctypes.data, self._threads(nthreads))
+        self._check(rc, "oracle_attn_fwd_local_rows")
         if rows is None:
             return out.reshape(B, Hq, S, D), lse.reshape(B, Hq, S)
         return out, lse

@@ -9,6 +9,10 @@
  * What it computes (sources are the four web pages on attention profiling):
  *   - The backward pass (gradients of q, k, v), derived from the forward
  *     definition below by the chain rule; see the backward section.
+ *   - A causal sliding-window mask (each query sees its own key and the
+ *     window - 1 keys before it), one of the special masks the ai-manual.ru
+ *     tutorial names (section 5's conclusions, section 7) as the reason to
+ *     write custom attention kernels.
  *   - The attention formula softmax(Q K^T / sqrt(d_k)) V, as stated in the
  *     "technical deep-dive" of the ainews.cool AttentionProfiler article.
  *   - The five-step causal pipeline of the Hugging Face "Profiling in PyTorch
@@ -77,6 +81,19 @@ static int64_t kv_head(const shape_t* sh, int64_t h) {
 #else
     return h / (sh->Hq / sh->Hkv);
 #endif
+}
+
+/* First visible key for query i under a causal sliding window of `window`
+ * keys (the query's own position and the window - 1 before it); window <= 0
+ * means no window. */
+static int64_t first_key(int64_t i, int64_t window) {
+    if (window <= 0) return 0;
+#if ORACLE_PLANT == 13
+    const int64_t f = i - window; /* planted: window one key too wide */
+#else
+    const int64_t f = i - window + 1;
+#endif
+    return f > 0 ? f : 0;
 }
 
 /* Last visible key for query i: i when causal (mask j > i), S-1 otherwise. */
@@ -165,6 +182,7 @@ typedef struct {
     shape_t sh;
     double scale;
     int causal;
+    int64_t window; /* > 0: causal sliding window of this many keys */
     const int64_t* rows;
     double *out, *lse;
 } attn_ctx;
@@ -176,7 +194,8 @@ typedef struct {
  *   l     = sum_j exp(s_j - m)
  *   out_d = sum_j exp(s_j - m) v[b,g,j,d] / l
  *   lse   = m + ln l
- * with g the key/value head of h and J(i) = {0..i} (causal) or {0..S-1}.
+ * with g the key/value head of h and J(i) = {0..i} (causal) or {0..S-1};
+ * with a sliding window of W keys, J(i) = {max(0, i-W+1)..i}.
  * Subtracting m changes nothing mathematically; it only keeps exp finite.
  */
 static void attn_row(void* vctx, int64_t n, double* s) {
@@ -191,9 +210,10 @@ static void attn_row(void* vctx, int64_t n, double* s) {
     const float* vb = c->v + (b * sh->Hkv + g) * S * D;
     double* o = c->out + n * D;
     const int64_t jl = last_key(sh, i, c->causal);
+    const int64_t j0 = first_key(i, c->window);
 
     double m = -INFINITY;
-    for (int64_t j = 0; j <= jl; ++j) {
+    for (int64_t j = j0; j <= jl; ++j) {
         const float* kj = kb + j * D;
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d) {
@@ -216,7 +236,7 @@ static void attn_row(void* vctx, int64_t n, double* s) {
         return;
     }
     double l = 0.0;
-    for (int64_t j = 0; j <= jl; ++j) {
+    for (int64_t j = j0; j <= jl; ++j) {
 #if ORACLE_PLANT == 4
         const double w = exp(m - s[j]); /* planted: sign flipped in the exponent */
 #else
@@ -240,6 +260,12 @@ static void attn_row(void* vctx, int64_t n, double* s) {
 #endif
 }
 
+int oracle_attn_fwd_local_rows(const float* q, const float* k, const float* v,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t S, int64_t D,
+                               double scale, int causal, int64_t window,
+                               const int64_t* rows, int64_t nrows,
+                               double* out, double* lse, int nthreads);
+
 /*
  * Attention forward for the listed rows.  rows[n] indexes the flattened
  * [B, Hq, S] row space; out is [nrows, D], lse is [nrows].
@@ -252,7 +278,23 @@ int oracle_attn_fwd_rows(const float* q, const float* k, const float* v,
                          double scale, int causal,
                          const int64_t* rows, int64_t nrows,
                          double* out, double* lse, int nthreads) {
+    return oracle_attn_fwd_local_rows(q, k, v, B, Hq, Hkv, S, D, scale, causal, 0, rows, nrows, out, lse,
+                                      nthreads);
+}
+
+/*
+ * As oracle_attn_fwd_rows, with a causal sliding window: query i sees keys
+ * max(0, i - window + 1) .. i.  window <= 0 means no window (then causal
+ * selects plain causal or full attention); window >= 1 requires causal = 1.
+ */
+int oracle_attn_fwd_local_rows(const float* q, const float* k, const float* v,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t S, int64_t D,
+                               double scale, int causal, int64_t window,
+                               const int64_t* rows, int64_t nrows,
+                               double* out, double* lse, int nthreads) {
     attn_ctx c;
+    if (window > 0 && !causal) return -2;
+    c.window = window;
     c.q = q; c.k = k; c.v = v;
     c.sh.B = B; c.sh.Hq = Hq; c.sh.Hkv = Hkv; c.sh.S = S; c.sh.D = D;
     c.scale = scale;

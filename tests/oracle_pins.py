@@ -21,6 +21,11 @@ What pins what:
     and logsumexp, rows sum to one, zero above the diagonal.
   step 5 (attn v): numpy matmul, exact integer products.
   composition: steps 1-5 chained equal the fused forward.
+  causal sliding window (one of the special masks the ai-manual.ru tutorial
+    names as the reason for custom kernels): window >= S equals causal,
+    window 1 gives out_i = v_i, each row equals the last row of the causal
+    attention over its own window, torch's float64 SDPA with an explicit band
+    mask.
   backward (chain-rule derivative of the forward; the ai-manual.ru tutorial,
   section 6, only warns that the flash backward is easy to get wrong):
     central finite differences of sum(dout * out) through the pinned forward
@@ -401,6 +406,74 @@ STEP_PINS = [pin_qk_numpy, pin_qk_integer, pin_golden_softmax, pin_softmax_scipy
              pin_pv_numpy, pin_pv_integer, pin_chain_equals_fused]
 
 # --------------------------------------------------------------------------
+# causal sliding window
+# --------------------------------------------------------------------------
+
+def pin_local_wide_is_causal(orc):
+    """A window of at least S keys hides nothing the causal mask shows."""
+    q = _randn((2, 4, 33, 16), 100)
+    k = _randn((2, 2, 33, 16), 101)
+    v = _randn((2, 2, 33, 16), 102)
+    out, lse = orc.attn_fwd(q, k, v, 0.25, True)
+    for w in (33, 34, 1000):
+        o2, l2 = orc.attn_fwd_local(q, k, v, 0.25, w)
+        _close(o2, out, 0.0, f"window {w} = causal out")
+        _close(l2, lse, 0.0, f"window {w} = causal lse")
+
+
+def pin_local_w1(orc):
+    """Window 1: every query sees only its own key, so out_i = v_i exactly and
+    lse_i = scale q_i . k_i."""
+    q = _randn((1, 2, 20, 8), 103)
+    k = _randn((1, 1, 20, 8), 104)
+    v = _randn((1, 1, 20, 8), 105)
+    out, lse = orc.attn_fwd_local(q, k, v, 0.5, 1)
+    _close(out, np.repeat(v, 2, axis=1).astype(np.float64), 0.0, "window 1 out")
+    ref = 0.5 * np.einsum("bhsd,bhsd->bhs", q.astype(np.float64), np.repeat(k, 2, axis=1).astype(np.float64))
+    _close(lse, ref, 1e-12, "window 1 lse")
+
+
+def pin_local_subproblem(orc):
+    """Row i with window W is the last row of causal attention over keys
+    i-W+1..i alone (the pinned causal forward on a shorter sequence)."""
+    B, H, S, D, W = 1, 2, 40, 8, 7
+    q = _randn((B, H, S, D), 106)
+    k = _randn((B, H, S, D), 107)
+    v = _randn((B, H, S, D), 108)
+    out, lse = orc.attn_fwd_local(q, k, v, 0.3, W)
+    for i in (0, 3, 6, 7, 20, S - 1):
+        lo = max(0, i - W + 1)
+        o2, l2 = orc.attn_fwd(q[:, :, lo:i + 1], k[:, :, lo:i + 1], v[:, :, lo:i + 1], 0.3, True)
+        _close(out[:, :, i], o2[:, :, -1], 1e-14, f"subproblem row {i}")
+        _close(lse[:, :, i], l2[:, :, -1], 1e-14, f"subproblem lse {i}")
+
+
+def pin_local_torch(orc):
+    """torch's float64 CPU scaled_dot_product_attention with an explicit band
+    mask (j <= i and j > i - W) agrees."""
+    import torch
+
+    B, Hq, Hkv, S, D = 2, 4, 2, 50, 16
+    q = _randn((B, Hq, S, D), 109)
+    k = _randn((B, Hkv, S, D), 110)
+    v = _randn((B, Hkv, S, D), 111)
+    sc = 1 / math.sqrt(D)
+    tq = torch.from_numpy(q.astype(np.float64))
+    tk = torch.from_numpy(k.astype(np.float64)).repeat_interleave(2, dim=1)
+    tv = torch.from_numpy(v.astype(np.float64)).repeat_interleave(2, dim=1)
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    for W in (1, 5, 16, 49):
+        band = (j <= i) & (j > i - W)
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=band, scale=sc)
+        out, _ = orc.attn_fwd_local(q, k, v, sc, W)
+        _close(out, ref.numpy(), 1e-12, f"torch band W={W}")
+
+
+LOCAL_PINS = [pin_local_wide_is_causal, pin_local_w1, pin_local_subproblem, pin_local_torch]
+
+
+# --------------------------------------------------------------------------
 # backward
 # --------------------------------------------------------------------------
 
@@ -517,4 +590,4 @@ def pin_bwd_special(orc):
 
 BWD_PINS = [pin_bwd_finite_diff, pin_bwd_torch, pin_bwd_invariants, pin_bwd_special]
 
-ALL_PINS = ATTN_PINS + STEP_PINS + BWD_PINS
+ALL_PINS = ATTN_PINS + STEP_PINS + LOCAL_PINS + BWD_PINS

@@ -27,6 +27,7 @@ PLANTS = {
     10: "backward dq uses v for k",
     11: "backward key pass mask flipped",
     12: "backward dk dv from one head of the group",
+    13: "sliding window one key too wide",
 }
 
 
