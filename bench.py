@@ -132,6 +132,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-local", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="seconds of untimed steps before the warmup steps (clock ramp-up)")
@@ -302,6 +303,25 @@ def main():
                "flops": bfl, "launches": 3}
         del do, gq, gk, gv, delta
 
+    # causal sliding window of 1024 keys on the same inputs (attn_fwd_local_bf16);
+    # FLOPs counted over the visible (query, key) pairs only
+    window = 1024
+    local = None
+    if not args.no_local:
+        def fused_local():
+            rc = _lib.attn_fwd_local_bf16(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(),
+                                          lse.data_ptr(), B, Hq, Hkv, S, D, sc, window, sp)
+            if rc:
+                raise _lib.AttnError(rc, "attn_fwd_local_bf16")
+
+        fused_local()
+        torch.cuda.synchronize()
+        lms = float(np.median(time_launches(fused_local, 10, stream)))
+        visible = sum(min(i + 1, window) for i in range(S))
+        lfl = 4.0 * B * Hq * D * visible
+        local = {"workload": f"causal sliding window W={window}, B4 H16 S4096 D128 bf16", "window": window,
+                 "ms": round(lms, 4), "tflops": round(lfl / (lms * 1e-3) / 1e12, 2), "flops": lfl}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(q, k, v, B, Hq, S, D, sc, seconds=args.cpu_seconds)
@@ -329,6 +349,7 @@ def main():
         "noncausal": noncausal,
         "unfused": unfused,
         "backward": bwd,
+        "local": local,
         "gpu": props.name,
         "cus": props.multi_processor_count,
         "timed_wall_s": round(wall, 4),

@@ -97,6 +97,21 @@ attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* 
                          void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Fused forward with a causal sliding window (bfloat16).
+ *
+ * As attn_fwd_bf16 with causal = 1, except that query i sees only keys
+ * max(0, i - window + 1) .. i: its own position and the window - 1 before it.
+ * Special masks like this one are what the ai-manual.ru tutorial gives as the
+ * reason to write custom attention kernels (section 5's conclusions,
+ * section 7).  Key tiles wholly before a query tile's window are skipped, as
+ * the causal mask skips tiles after the diagonal.  window >= S gives exactly
+ * the causal result.  window < 1 returns ATTN_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+attn_status attn_fwd_local_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
+                                int B, int Hq, int Hkv, int S, int D, float scale, int window,
+                                void* stream);
+
+/* ---------------------------------------------------------------------------
  * Unfused trio, mirroring the naive pipeline one step per kernel.
  *
  * Step 1, attn_qk_gemm_*: scores[b,h,i,j] = q[b,h,i,:] . k[b,g,j,:] for every

@@ -40,11 +40,12 @@ def _raise(code: int, name: str):
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = True, scale: float | None = None,
-        out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True):
+        out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True, window: int | None = None):
     """Fused attention forward.  q ``[B,Hq,S,D]``, k/v ``[B,Hkv,S,D]``, bf16 or fp32.
 
     Returns ``(out, lse)``; ``lse`` is float32 ``[B,Hq,S]`` (None if ``lse=False``).
-    ``scale`` defaults to 1/sqrt(D).
+    ``scale`` defaults to 1/sqrt(D).  ``window`` (bf16, causal only): each query
+    sees its own key and the ``window - 1`` before it (``attn_fwd_local_bf16``).
     """
     if q.dtype not in _SUFFIX:
         raise TypeError(f"unsupported dtype {q.dtype}")
@@ -66,8 +67,16 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Tru
         lse = None
     elif lse is not None:
         _check(lse, "lse", torch.float32, 3)
+    lp = lse.data_ptr() if lse is not None else None
+    if window is not None:
+        if q.dtype != torch.bfloat16 or not causal:
+            raise ValueError("a sliding window needs bf16 tensors and causal=True")
+        code = _lib.attn_fwd_local_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lp,
+                                        B, Hq, Hkv, S, D, float(scale), int(window), _stream(q.device))
+        _raise(code, "attn_fwd_local_bf16")
+        return out, lse
     fn = getattr(_lib, "attn_fwd_" + _SUFFIX[q.dtype])
-    code = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+    code = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lp,
               B, Hq, Hkv, S, D, float(scale), int(bool(causal)), _stream(q.device))
     _raise(code, "attn_fwd_" + _SUFFIX[q.dtype])
     return out, lse

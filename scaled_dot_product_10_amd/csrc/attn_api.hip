@@ -162,6 +162,7 @@ attn::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* out, f
     a.D = D;
     a.scale = scale;
     a.causal = causal;
+    a.window = 0;
     return a;
 }
 
@@ -175,6 +176,16 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* out
     if (st != ATTN_OK) return st;
     return hip_status(attn::launch_fwd_bf16(fwd_args(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal),
                                             (hipStream_t)stream));
+}
+
+attn_status attn_fwd_local_bf16(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+                                int Hkv, int S, int D, float scale, int window, void* stream) {
+    const attn_status st = check_fwd(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, 1, 2);
+    if (st != ATTN_OK) return st;
+    if (window < 1) return ATTN_ERR_UNSUPPORTED;
+    attn::FwdArgs a = fwd_args(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, 1);
+    a.window = window;
+    return hip_status(attn::launch_fwd_bf16(a, (hipStream_t)stream));
 }
 
 attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse, int B, int Hq,

@@ -62,6 +62,7 @@ struct Params {
     uint32_t total;
     uint32_t hgrp;  // causal: heads whose tiles one XCD runs together (0: plain order)
     float c;        // scale * log2(e), > 0
+    int window;     // LOCAL: keys each query sees (its own and window - 1 before it)
 };
 
 // Workgroups one XCD holds at once: 32 CUs per XCD, one 8-wave workgroup per CU.
@@ -150,8 +151,13 @@ __device__ __forceinline__ void phase_barrier(bool wait_dma) {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool CAUSAL>
+// LOCAL (with CAUSAL): sliding window, query i sees keys i - window + 1 .. i.
+// The workgroup starts at the first key tile its first query sees; tiles
+// before a wave's own window are multiplied and fully masked, which keeps the
+// phase schedule identical to the causal one.
+template <int D, bool CAUSAL, bool LOCAL>
 __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
+    static_assert(!LOCAL || CAUSAL, "a sliding window is a causal mask");
     using T = Tile<D>;
     constexpr int KS = D / 16;  // k-steps of the Q.K^T product
     constexpr int DB = D / 32;  // 32-row blocks of O^T
@@ -210,15 +216,16 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     const int qlast = min(m0 + BM, S) - 1;
     const int ntiles = (S + BN - 1) / BN;
     const int nend = CAUSAL ? min(ntiles, qlast / BN + 1) : ntiles;
+    const int nbeg = LOCAL ? max(0, m0 - p.window + 1) / BN : 0;
 
-    // ---- prologue: K(0), V(0), K(1) in flight while Q is loaded -------------
+    // ---- prologue: K(nbeg), V(nbeg), K(nbeg+1) in flight while Q is loaded --
     DmaPlan<D, false> kdma;
     DmaPlan<D, true> vdma;
     kdma.init(wave, lane);
     vdma.init(wave, lane);
-    kdma.issue(kb, 0, S, Kbuf(0), wave);
-    vdma.issue(vb, 0, S, Vbuf(0), wave);
-    if (nend > 1) kdma.issue(kb, BN, S, Kbuf(1), wave);
+    kdma.issue(kb, nbeg * BN, S, Kbuf(nbeg), wave);
+    vdma.issue(vb, nbeg * BN, S, Vbuf(nbeg), wave);
+    if (nbeg + 1 < nend) kdma.issue(kb, (nbeg + 1) * BN, S, Kbuf(nbeg + 1), wave);
 
     // Q operand (B of S^T = K.Q^T): query qi, d = 16*ks + 8*g .. +7.
     bf16x8 qreg[KS];
@@ -337,13 +344,13 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     // one reference), moves m, rescales O and l by 2^((m_old - m_new) c) and
     // redoes the exponentials, after which every p <= 1.
     auto softmax_impl = [&](int n0, auto may_mask) __attribute__((always_inline)) {
-        if (may_mask && ((CAUSAL && n0 + BN - 1 > qwmin) || n0 + BN > S)) {
+        if (may_mask && ((CAUSAL && n0 + BN - 1 > qwmin) || n0 + BN > S || (LOCAL && n0 <= qwmax - p.window))) {
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = n0 + sb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    if ((CAUSAL && key > qi) || key >= S) sacc[sb][r] = -INFINITY;
+                    if ((CAUSAL && key > qi) || key >= S || (LOCAL && key <= qi - p.window)) sacc[sb][r] = -INFINITY;
                 }
             }
         }
@@ -432,9 +439,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     // V(k-2), whose last readers finished in phase 2k-1, and is awaited before
     // the barrier that ends phase 2k+1.
     if (grp == 0) {
-        qk(Kbuf(0));
+        qk(Kbuf(nbeg));
         phase_barrier(false);
-        for (int n = 0; n < nend; ++n) {
+        for (int n = nbeg; n < nend; ++n) {
             vphase(n);
             phase_barrier(true);
             dma_step(n + 1);
@@ -444,9 +451,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
         phase_barrier(true);
     } else {
         phase_barrier(false);
-        qk(Kbuf(0));
+        qk(Kbuf(nbeg));
         phase_barrier(true);
-        for (int n = 0; n < nend; ++n) {
+        for (int n = nbeg; n < nend; ++n) {
             dma_step(n + 1);
             vphase(n);
             phase_barrier(false);
@@ -475,11 +482,12 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool LOCAL = false>
 hipError_t launch(const Params& prm, hipStream_t stream) {
     Params arg = prm;
     void* args[] = {&arg};
-    return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, CAUSAL>, dim3(prm.total), dim3(NT), args, 0, stream);
+    return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, CAUSAL, LOCAL>, dim3(prm.total), dim3(NT), args, 0,
+                           stream);
 }
 
 }  // namespace
@@ -498,6 +506,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     prm.nq = (a.S + BM - 1) / BM;
     prm.total = (uint32_t)((int64_t)a.B * a.Hq * prm.nq);
     prm.c = a.scale * kLog2e;
+    prm.window = a.window;
     prm.hgrp = 0;
     const uint32_t per = prm.total / 8u;
     if (per > 0 && per % (uint32_t)prm.nq == 0) {
@@ -507,6 +516,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
         while (heads_here % g) --g;
         prm.hgrp = g;
     }
+    // a window of at least S keys hides nothing the causal mask shows
+    if (a.causal && a.window > 0 && a.window < a.S)
+        return a.D == 128 ? launch<128, true, true>(prm, stream) : launch<64, true, true>(prm, stream);
     if (a.D == 128) return a.causal ? launch<128, true>(prm, stream) : launch<128, false>(prm, stream);
     return a.causal ? launch<64, true>(prm, stream) : launch<64, false>(prm, stream);
 }

@@ -16,6 +16,7 @@ struct FwdArgs {
     int B, Hq, Hkv, S, D;
     float scale;  // > 0, finite
     int causal;   // 0 or 1
+    int window;   // 0: none; >= 1 (bf16, causal only): sliding window of this many keys
 };
 
 struct QkArgs {

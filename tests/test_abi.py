@@ -40,7 +40,7 @@ def L():
 
 def test_header_symbols_are_exported(L):
     syms = header_symbols()
-    assert len(syms) == 14, syms
+    assert len(syms) == 15, syms
     nm = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)], capture_output=True, text=True,
                         check=True).stdout
     exported = set(re.findall(r"\bT (\w+)$", nm, flags=re.M))
@@ -101,6 +101,16 @@ def fwd_args(**kw):
 ])
 def test_fwd_rejects(fn, kw, code):
     assert fn(*fwd_args(**kw)) == code
+
+
+def test_local_rejects():
+    f = _lib.attn_fwd_local_bf16
+    args = [A, Bp, C, Dp, E, 1, 2, 1, 16, 64, 0.125]
+    assert f(*args, 0, None) == UNSUP
+    assert f(*args, -3, None) == UNSUP
+    assert f(None, *args[1:], 4, None) == NULL
+    assert f(A, Bp, C, A, E, 1, 2, 1, 16, 64, 0.125, 4, None) == ALIAS
+    assert f(A, Bp, C, Dp, E, 1, 2, 1, 16, 64, float("nan"), 4, None) == SCALE
 
 
 def test_qk_rejects():
