@@ -16,6 +16,8 @@ profiling; each function's C counterpart states the definition it writes out):
 * ``attn_fwd_local`` -- the same with a causal sliding window (query i sees
   its own key and the window - 1 before it): one of the special masks that
   the ai-manual.ru tutorial names as the reason for custom kernels.
+* ``attn_fwd_kv`` -- Sq queries against Skv >= Sq keys and values, the
+  queries being the last Sq positions (a decode step; the split-KV path).
 * ``qk_scores``  -- step 1 of that pipeline (q k^T, unscaled).
 * ``masked_softmax`` -- steps 2-4 (scale, mask with -inf, softmax).
 * ``pv``         -- step 5 (attn v).
@@ -64,8 +66,8 @@ class Oracle:
 
     def __init__(self, path: Path = LIB):
         path = Path(path)
-        if not path.exists():
-            compile_oracle(path)
+        if not path.exists() or (path == LIB and path.stat().st_mtime < SRC.stat().st_mtime):
+            compile_oracle(path)  # missing, or older than its source
         self.path = path
         self.lib = ctypes.CDLL(str(path))
         L = self.lib
@@ -77,6 +79,10 @@ class Oracle:
         L.oracle_attn_fwd_local_rows.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64,
                                                  ctypes.c_double, ctypes.c_int, _i64, _ptr, _i64, _ptr,
                                                  _ptr, ctypes.c_int]
+        L.oracle_attn_fwd_kv_rows.restype = ctypes.c_int
+        L.oracle_attn_fwd_kv_rows.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64,
+                                              ctypes.c_double, ctypes.c_int, _ptr, _i64, _ptr, _ptr,
+                                              ctypes.c_int]
         L.oracle_qk_scores_rows.restype = ctypes.c_int
         L.oracle_qk_scores_rows.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _ptr, _i64,
                                             _ptr, ctypes.c_int]
@@ -163,6 +169,26 @@ class Oracle:
         self._check(rc, "oracle_attn_fwd_local_rows")
         if rows is None:
             return out.reshape(B, Hq, S, D), lse.reshape(B, Hq, S)
+        return out, lse
+
+    def attn_fwd_kv(self, q, k, v, scale: float, causal: bool, rows=None, nthreads=None):
+        """q ``[B,Hq,Sq,D]`` against k, v ``[B,Hkv,Skv,D]`` (Sq <= Skv): the queries
+        are the last Sq positions, so causal query i sees keys 0..Skv-Sq+i.
+        Returns out ``[B,Hq,Sq,D]``, lse ``[B,Hq,Sq]`` (or per listed row)."""
+        q, k, v = self._f32(q), self._f32(k), self._f32(v)
+        B, Hq, Sq, D = q.shape
+        Hkv, Skv = k.shape[1], k.shape[2]
+        assert k.shape == (B, Hkv, Skv, D) and v.shape == k.shape
+        r = self._rows(rows, B * Hq * Sq)
+        out = np.empty((r.size, D), dtype=np.float64)
+        lse = np.empty((r.size,), dtype=np.float64)
+        rc = self.lib.oracle_attn_fwd_kv_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                              B, Hq, Hkv, Sq, Skv, D, float(scale), int(bool(causal)),
+                                              r.ctypes.data, r.size, out.ctypes.data, lse.ctypes.data,
+                                              self._threads(nthreads))
+        self._check(rc, "oracle_attn_fwd_kv_rows")
+        if rows is None:
+            return out.reshape(B, Hq, Sq, D), lse.reshape(B, Hq, Sq)
         return out, lse
 
     # -- unfused steps ------------------------------------------------------

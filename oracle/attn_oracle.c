@@ -9,6 +9,9 @@
  * What it computes (sources are the four web pages on attention profiling):
  *   - The backward pass (gradients of q, k, v), derived from the forward
  *     definition below by the chain rule; see the backward section.
+ *   - Queries against a longer key/value sequence (a decode step against a
+ *     key/value cache, computed by the split-KV path): the queries are the
+ *     last Sq of the Skv positions.
  *   - A causal sliding-window mask (each query sees its own key and the
  *     window - 1 keys before it), one of the special masks the ai-manual.ru
  *     tutorial names (section 5's conclusions, section 7) as the reason to
@@ -307,6 +310,85 @@ int oracle_attn_fwd_local_rows(const float* q, const float* k, const float* v,
     rc = check_rows(&c.sh, rows, nrows);
     if (rc) return rc;
     return run_rows(attn_row, &c, nrows, S, nthreads);
+}
+
+/* ------------------------------------------------------------------------ */
+/* queries against a longer key/value sequence (decode, split-KV)            */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const float *q, *k, *v;
+    int64_t B, Hq, Hkv, Sq, Skv, D;
+    double scale;
+    int causal;
+    const int64_t* rows;
+    double *out, *lse;
+} kv_ctx;
+
+/*
+ * Query i of Sq (0-based) is the sequence position Skv - Sq + i: the queries
+ * are the last Sq positions of a sequence whose keys and values are all Skv
+ * positions (a decode step against a key/value cache).  Causal: it sees keys
+ * 0 .. Skv - Sq + i; otherwise all Skv keys.  Then the same definition as
+ * attn_row: s_j = scale q_i . k_j, out = sum_j exp(s_j - m) v_j / l,
+ * lse = m + ln l.
+ */
+static void kv_row(void* vctx, int64_t n, double* s) {
+    const kv_ctx* c = (const kv_ctx*)vctx;
+    const int64_t r = c->rows[n];
+    const int64_t i = r % c->Sq, bh = r / c->Sq;
+    const int64_t h = bh % c->Hq, b = bh / c->Hq;
+    const int64_t g = h / (c->Hq / c->Hkv);
+    const int64_t D = c->D;
+    const float* qi = c->q + r * D;
+    const float* kb = c->k + (b * c->Hkv + g) * c->Skv * D;
+    const float* vb = c->v + (b * c->Hkv + g) * c->Skv * D;
+    double* o = c->out + n * D;
+#if ORACLE_PLANT == 14
+    const int64_t jl = c->causal ? i : c->Skv - 1; /* planted: top-left alignment */
+#else
+    const int64_t jl = c->causal ? c->Skv - c->Sq + i : c->Skv - 1;
+#endif
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= jl; ++j) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += (double)qi[d] * (double)kb[j * D + d];
+        s[j] = c->scale * dot;
+        if (s[j] > m) m = s[j];
+    }
+    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+    double l = 0.0;
+    for (int64_t j = 0; j <= jl; ++j) {
+        const double w = exp(s[j] - m);
+        l += w;
+        for (int64_t d = 0; d < D; ++d) o[d] += w * (double)vb[j * D + d];
+    }
+    for (int64_t d = 0; d < D; ++d) o[d] /= l;
+    c->lse[n] = m + log(l);
+}
+
+/*
+ * Attention of q [B, Hq, Sq, D] against k, v [B, Hkv, Skv, D] for the listed
+ * rows of the flattened [B, Hq, Sq] space; out [nrows, D], lse [nrows].
+ * Requires 1 <= Sq <= Skv.
+ */
+int oracle_attn_fwd_kv_rows(const float* q, const float* k, const float* v,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                            double scale, int causal, const int64_t* rows, int64_t nrows,
+                            double* out, double* lse, int nthreads) {
+    kv_ctx c;
+    c.q = q; c.k = k; c.v = v;
+    c.B = B; c.Hq = Hq; c.Hkv = Hkv; c.Sq = Sq; c.Skv = Skv; c.D = D;
+    c.scale = scale;
+    c.causal = causal ? 1 : 0;
+    c.rows = rows;
+    c.out = out;
+    c.lse = lse;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < Sq || D < 1 || Hq % Hkv != 0) return -2;
+    const int64_t total = B * Hq * Sq;
+    for (int64_t n = 0; n < nrows; ++n)
+        if (rows[n] < 0 || rows[n] >= total) return -3;
+    return run_rows(kv_row, &c, nrows, Skv, nthreads);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -26,6 +26,10 @@ What pins what:
     window 1 gives out_i = v_i, each row equals the last row of the causal
     attention over its own window, torch's float64 SDPA with an explicit band
     mask.
+  queries against a longer key/value sequence (decode, split-KV): Sq = Skv
+    equals the square forward, each query row equals the square causal
+    forward's row at its position, and torch's float64 SDPA with an explicit
+    bottom-right mask.
   backward (chain-rule derivative of the forward; the ai-manual.ru tutorial,
   section 6, only warns that the flash backward is easy to get wrong):
     central finite differences of sum(dout * out) through the pinned forward
@@ -474,6 +478,61 @@ LOCAL_PINS = [pin_local_wide_is_causal, pin_local_w1, pin_local_subproblem, pin_
 
 
 # --------------------------------------------------------------------------
+# queries against a longer key/value sequence
+# --------------------------------------------------------------------------
+
+def pin_kv_square(orc):
+    """Sq = Skv is the square forward, causal and not, bit for bit."""
+    q = _randn((2, 4, 21, 8), 120)
+    k = _randn((2, 2, 21, 8), 121)
+    v = _randn((2, 2, 21, 8), 122)
+    for causal in (True, False):
+        a, la = orc.attn_fwd(q, k, v, 0.35, causal)
+        b, lb = orc.attn_fwd_kv(q, k, v, 0.35, causal)
+        _close(b, a, 0.0, f"kv square out causal={causal}")
+        _close(lb, la, 0.0, f"kv square lse causal={causal}")
+
+
+def pin_kv_suffix_rows(orc):
+    """Query i of Sq is position Skv-Sq+i: with the earlier positions filled
+    in, the square causal forward's rows Skv-Sq.. equal the decode rows."""
+    B, Hq, Hkv, Skv, D = 1, 4, 2, 50, 16
+    full_q = _randn((B, Hq, Skv, D), 123)
+    k = _randn((B, Hkv, Skv, D), 124)
+    v = _randn((B, Hkv, Skv, D), 125)
+    sq_out, sq_lse = orc.attn_fwd(full_q, k, v, 0.25, True)
+    for Sq in (1, 3, 17):
+        out, lse = orc.attn_fwd_kv(full_q[:, :, Skv - Sq:], k, v, 0.25, True)
+        _close(out, sq_out[:, :, Skv - Sq:], 1e-15, f"suffix rows Sq={Sq}")
+        _close(lse, sq_lse[:, :, Skv - Sq:], 1e-15, f"suffix lse Sq={Sq}")
+        nc, _ = orc.attn_fwd_kv(full_q[:, :, Skv - Sq:], k, v, 0.25, False)
+        _close(nc[:, :, -1], sq_out[:, :, -1], 1e-15, "last row sees every key")
+
+
+def pin_kv_torch(orc):
+    """torch's float64 CPU SDPA with an explicit bottom-right causal mask."""
+    import torch
+
+    B, Hq, Hkv, Sq, Skv, D = 2, 6, 3, 5, 37, 16
+    q = _randn((B, Hq, Sq, D), 126)
+    k = _randn((B, Hkv, Skv, D), 127)
+    v = _randn((B, Hkv, Skv, D), 128)
+    sc = 1 / math.sqrt(D)
+    tq = torch.from_numpy(q.astype(np.float64))
+    tk = torch.from_numpy(k.astype(np.float64)).repeat_interleave(2, dim=1)
+    tv = torch.from_numpy(v.astype(np.float64)).repeat_interleave(2, dim=1)
+    mask = torch.arange(Skv)[None, :] <= (Skv - Sq + torch.arange(Sq))[:, None]
+    for causal in (True, False):
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask if causal else None,
+                                                               scale=sc)
+        out, _ = orc.attn_fwd_kv(q, k, v, sc, causal)
+        _close(out, ref.numpy(), 1e-12, f"torch kv causal={causal}")
+
+
+KV_PINS = [pin_kv_square, pin_kv_suffix_rows, pin_kv_torch]
+
+
+# --------------------------------------------------------------------------
 # backward
 # --------------------------------------------------------------------------
 
@@ -590,4 +649,4 @@ def pin_bwd_special(orc):
 
 BWD_PINS = [pin_bwd_finite_diff, pin_bwd_torch, pin_bwd_invariants, pin_bwd_special]
 
-ALL_PINS = ATTN_PINS + STEP_PINS + LOCAL_PINS + BWD_PINS
+ALL_PINS = ATTN_PINS + STEP_PINS + LOCAL_PINS + KV_PINS + BWD_PINS

@@ -28,6 +28,7 @@ PLANTS = {
     11: "backward key pass mask flipped",
     12: "backward dk dv from one head of the group",
     13: "sliding window one key too wide",
+    14: "decode queries aligned top-left",
 }
 
 
