@@ -112,6 +112,31 @@ attn_status attn_fwd_local_bf16(const void* q, const void* k, const void* v, voi
                                 void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Split-KV forward for short query counts (bfloat16): a decode step.
+ *
+ * q, out: [B, Hq, Sq, D]; k, v: [B, Hkv, Skv, D] with 1 <= Sq <= Skv.  The
+ * queries are the last Sq positions of the sequence whose keys and values are
+ * given, so with causal = 1 query i sees keys 0 .. Skv - Sq + i (with Sq = 1,
+ * every key, as with causal = 0).  Otherwise the same operation as
+ * attn_fwd_bf16; lse [B, Hq, Sq] float32 or NULL.
+ * The key axis is cut into nsplit ranges processed in parallel (the "split-k"
+ * that the ai-manual.ru tutorial, section 4, lists as missing from its sketch
+ * kernel), then merged with the ranges' log-sum-exps.  workspace: float32,
+ * attn_splitkv_workspace_bytes(B, Hq, Sq, D, nsplit) bytes, 16-byte aligned,
+ * caller-owned, overwritten.  nsplit in 1..4096 (ATTN_ERR_UNSUPPORTED
+ * otherwise); attn_splitkv_default_splits suggests one.  Two kernel launches.
+ * ------------------------------------------------------------------------- */
+attn_status attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
+                                  float* workspace, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                                  float scale, int causal, int nsplit, void* stream);
+/* Workspace bytes for attn_fwd_splitkv_bf16: nsplit*B*Hq*Sq*(D+1)*4, or 0 on a
+ * bad size. */
+size_t attn_splitkv_workspace_bytes(int B, int Hq, int Sq, int D, int nsplit);
+/* A split count that gives about two workgroups per compute unit, or 0 on a
+ * bad size. */
+int attn_splitkv_default_splits(int B, int Hq, int Hkv, int Sq, int Skv);
+
+/* ---------------------------------------------------------------------------
  * Unfused trio, mirroring the naive pipeline one step per kernel.
  *
  * Step 1, attn_qk_gemm_*: scores[b,h,i,j] = q[b,h,i,:] . k[b,g,j,:] for every

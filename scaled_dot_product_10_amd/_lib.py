@@ -39,6 +39,9 @@ SIGNATURES = {
     "attn_masked_softmax_f32": (_i, [_p, _p, _p, _i, _i, _i, _f, _i, _p]),
     "attn_pv_gemm_bf16": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "attn_pv_gemm_f32": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p]),
+    "attn_fwd_splitkv_bf16": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _i, _p]),
+    "attn_splitkv_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
+    "attn_splitkv_default_splits": (_i, [_i, _i, _i, _i, _i]),
     "attn_bwd_bf16": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i]),
     "attn_scores_bytes": (ctypes.c_size_t, [_i, _i, _i]),
@@ -114,6 +117,20 @@ def attn_pv_gemm_bf16(p, v, out, B, Hq, Hkv, S, D, stream) -> int:
 
 def attn_pv_gemm_f32(p, v, out, B, Hq, Hkv, S, D, stream) -> int:
     return _call("attn_pv_gemm_f32", p, v, out, B, Hq, Hkv, S, D, stream)
+
+
+def attn_fwd_splitkv_bf16(q, k, v, out, lse, workspace, B, Hq, Hkv, Sq, Skv, D, scale, causal, nsplit,
+                          stream) -> int:
+    return _call("attn_fwd_splitkv_bf16", q, k, v, out, lse, workspace, B, Hq, Hkv, Sq, Skv, D, scale, causal,
+                 nsplit, stream)
+
+
+def attn_splitkv_workspace_bytes(B, Hq, Sq, D, nsplit) -> int:
+    return int(lib().attn_splitkv_workspace_bytes(B, Hq, Sq, D, nsplit))
+
+
+def attn_splitkv_default_splits(B, Hq, Hkv, Sq, Skv) -> int:
+    return int(lib().attn_splitkv_default_splits(B, Hq, Hkv, Sq, Skv))
 
 
 def attn_bwd_bf16(q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, S, D, scale, causal, stream) -> int:

@@ -182,3 +182,46 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, ls
                               B, Hq, Hkv, S, D, float(scale), int(bool(causal)), _stream(q.device))
     _raise(code, "attn_bwd_bf16")
     return dq, dk, dv
+
+
+def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = True,
+                scale: float | None = None, nsplit: int | None = None, workspace: torch.Tensor | None = None,
+                out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True):
+    """Split-KV forward (bf16): q ``[B,Hq,Sq,D]`` against k, v ``[B,Hkv,Skv,D]``
+    with Sq <= Skv; the queries are the last Sq positions (a decode step).
+
+    Returns ``(out, lse)``.  ``nsplit`` defaults to the library's suggestion;
+    ``workspace`` (float32, ``attn_splitkv_workspace_bytes`` bytes) is
+    allocated when absent.
+    """
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, n, torch.bfloat16)
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Skv, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k/v shapes {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if nsplit is None:
+        nsplit = _lib.attn_splitkv_default_splits(B, Hq, Hkv, Sq, Skv)
+    nbytes = _lib.attn_splitkv_workspace_bytes(B, Hq, Sq, D, nsplit)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 4) // 4,), device=q.device, dtype=torch.float32)
+    elif workspace.dtype != torch.float32 or workspace.numel() * 4 < nbytes or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be contiguous float32 of at least {nbytes} bytes")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16)
+    if lse is True:
+        lse = torch.empty((B, Hq, Sq), device=q.device, dtype=torch.float32)
+    elif lse is False:
+        lse = None
+    elif lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+    code = _lib.attn_fwd_splitkv_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
+                                      B, Hq, Hkv, Sq, Skv, D, float(scale), int(bool(causal)), int(nsplit),
+                                      _stream(q.device))
+    _raise(code, "attn_fwd_splitkv_bf16")
+    return out, lse

@@ -277,6 +277,74 @@ attn_status attn_pv_gemm_f32(const float* p, const float* v, float* out, int B, 
     return pv_common(p, v, out, B, Hq, Hkv, S, D, stream, 4);
 }
 
+constexpr int kMaxSplits = 4096;
+
+int64_t splitkv_ws_floats(int B, int Hq, int Sq, int D, int nsplit) {
+    return prod({nsplit, B, Hq, Sq, D + 1});
+}
+
+attn_status attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
+                                  float* workspace, int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                                  int causal, int nsplit, void* stream) {
+    if (!q || !k || !v || !out || !workspace) return ATTN_ERR_NULL_POINTER;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < Sq || Hq % Hkv != 0) return ATTN_ERR_BAD_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return ATTN_ERR_UNSUPPORTED;
+    if (nsplit < 1 || nsplit > kMaxSplits) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_BAD_SCALE;
+    const int64_t nq = prod({B, Hq, Sq, D, 2});
+    const int64_t nkv = prod({B, Hkv, Skv, D, 2});
+    const int64_t nl = prod({B, Hq, Sq, 4});
+    const int64_t nws = splitkv_ws_floats(B, Hq, Sq, D, nsplit);
+    if (nq < 0 || nkv < 0 || nl < 0 || nws < 0 || nws > (int64_t(1) << 60) / 4) return ATTN_ERR_BAD_SHAPE;
+    if (prod({B, Hkv, attn::splitkv_row_blocks(Hq, Hkv, Sq), nsplit}) > kMaxGrid ||
+        prod({B, Hq, Sq, D}) > kMaxGrid * 256LL)
+        return ATTN_ERR_BAD_SHAPE;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
+        misaligned(workspace, 16) || misaligned(lse, 4))
+        return ATTN_ERR_MISALIGNED;
+    const int64_t nwb = nws * 4;
+    if (overlap(out, nq, q, nq) || overlap(out, nq, k, nkv) || overlap(out, nq, v, nkv) ||
+        overlap(lse, nl, q, nq) || overlap(lse, nl, k, nkv) || overlap(lse, nl, v, nkv) || overlap(lse, nl, out, nq) ||
+        overlap(workspace, nwb, q, nq) || overlap(workspace, nwb, k, nkv) || overlap(workspace, nwb, v, nkv) ||
+        overlap(workspace, nwb, out, nq) || overlap(workspace, nwb, lse, nl))
+        return ATTN_ERR_ALIAS;
+    attn::SplitKvArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.workspace = workspace;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Sq = Sq;
+    a.Skv = Skv;
+    a.D = D;
+    a.scale = scale;
+    a.causal = causal;
+    a.nsplit = nsplit;
+    return hip_status(attn::launch_splitkv_bf16(a, (hipStream_t)stream));
+}
+
+size_t attn_splitkv_workspace_bytes(int B, int Hq, int Sq, int D, int nsplit) {
+    if (nsplit < 1 || nsplit > kMaxSplits || (D != 64 && D != 128)) return 0;
+    const int64_t n = splitkv_ws_floats(B, Hq, Sq, D, nsplit);
+    return n < 0 || n > (int64_t(1) << 60) / 4 ? 0 : (size_t)n * 4;
+}
+
+int attn_splitkv_default_splits(int B, int Hq, int Hkv, int Sq, int Skv) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || Hq % Hkv != 0) return 0;
+    // about two workgroups per compute unit (256 CUs), at least one key chunk per split
+    const int64_t units = (int64_t)B * Hkv * attn::splitkv_row_blocks(Hq, Hkv, Sq);
+    const int64_t want = (512 + units - 1) / units;
+    const int64_t chunks = (Skv + attn::splitkv_chunk() - 1) / attn::splitkv_chunk();
+    int64_t n = want < chunks ? want : chunks;
+    if (n > kMaxSplits) n = kMaxSplits;
+    return (int)(n < 1 ? 1 : n);
+}
+
 attn_status attn_bwd_bf16(const void* q, const void* k, const void* v, const void* out, const void* dout,
                           const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv,
                           int S, int D, float scale, int causal, void* stream) {

@@ -1,6 +1,6 @@
 // Internal launchers behind the C ABI (include/attn.h).  Arguments are
 // already validated by the caller; each launcher enqueues exactly one kernel,
-// except the backward's, which enqueues three.
+// except the backward's (three) and the split-KV forward's (two).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -58,6 +58,19 @@ struct BwdArgs {
     int causal;
 };
 
+struct SplitKvArgs {
+    const void* q;     // [B, Hq, Sq, D]
+    const void* k;     // [B, Hkv, Skv, D]
+    const void* v;
+    void* out;         // [B, Hq, Sq, D]
+    float* lse;        // [B, Hq, Sq] or null
+    float* workspace;  // nsplit * B*Hq*Sq * (D + 1) floats
+    int B, Hq, Hkv, Sq, Skv, D;
+    float scale;
+    int causal;
+    int nsplit;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_qk_gemm_bf16(const QkArgs& a, hipStream_t stream);
@@ -66,6 +79,9 @@ hipError_t launch_masked_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream);
 hipError_t launch_masked_softmax_f32(const SoftmaxArgs& a, hipStream_t stream);
 hipError_t launch_pv_gemm_bf16(const PvArgs& a, hipStream_t stream);
 hipError_t launch_pv_gemm_f32(const PvArgs& a, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);  // three kernels
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);          // three kernels
+hipError_t launch_splitkv_bf16(const SplitKvArgs& a, hipStream_t stream);  // two kernels
+int splitkv_row_blocks(int Hq, int Hkv, int Sq);  // workgroups per (b, kv head) and split
+int splitkv_chunk();                              // keys per workgroup step
 
 }  // namespace attn

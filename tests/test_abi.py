@@ -40,7 +40,7 @@ def L():
 
 def test_header_symbols_are_exported(L):
     syms = header_symbols()
-    assert len(syms) == 15, syms
+    assert len(syms) == 18, syms
     nm = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)], capture_output=True, text=True,
                         check=True).stdout
     exported = set(re.findall(r"\bT (\w+)$", nm, flags=re.M))
@@ -111,6 +111,38 @@ def test_local_rejects():
     assert f(None, *args[1:], 4, None) == NULL
     assert f(A, Bp, C, A, E, 1, 2, 1, 16, 64, 0.125, 4, None) == ALIAS
     assert f(A, Bp, C, Dp, E, 1, 2, 1, 16, 64, float("nan"), 4, None) == SCALE
+
+
+def test_splitkv_rejects_and_sizes():
+    f = _lib.attn_fwd_splitkv_bf16
+    ws = E + (1 << 30)
+
+    def call(**kw):
+        a = dict(q=A, k=Bp, v=C, out=Dp, lse=E, ws=ws, B=1, Hq=4, Hkv=2, Sq=1, Skv=100, D=128, scale=0.1, causal=1,
+                 nsplit=4, stream=None)
+        a.update(kw)
+        return f(*[a[n] for n in ("q", "k", "v", "out", "lse", "ws", "B", "Hq", "Hkv", "Sq", "Skv", "D", "scale",
+                                  "causal", "nsplit", "stream")])
+
+    assert call(ws=None) == NULL
+    assert call(q=None) == NULL
+    assert call(Sq=101) == SHAPE
+    assert call(Sq=0) == SHAPE
+    assert call(Hq=3) == SHAPE
+    assert call(D=80) == UNSUP
+    assert call(nsplit=0) == UNSUP
+    assert call(nsplit=5000) == UNSUP
+    assert call(causal=2) == UNSUP
+    assert call(scale=-1.0) == SCALE
+    assert call(ws=ws + 4) == ALIGN
+    assert call(ws=A) == ALIAS
+    assert call(out=Bp) == ALIAS
+    assert _lib.attn_splitkv_workspace_bytes(2, 8, 3, 128, 5) == 5 * 2 * 8 * 3 * 129 * 4
+    assert _lib.attn_splitkv_workspace_bytes(2, 8, 3, 100, 5) == 0
+    assert _lib.attn_splitkv_workspace_bytes(2, 8, 3, 128, 0) == 0
+    assert _lib.attn_splitkv_default_splits(8, 32, 8, 1, 4096) == 8     # 64 units -> 8 splits
+    assert _lib.attn_splitkv_default_splits(1, 1, 1, 1, 100) == 1       # one 128-key chunk
+    assert _lib.attn_splitkv_default_splits(1, 4, 3, 1, 100) == 0
 
 
 def test_qk_rejects():
