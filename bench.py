@@ -133,6 +133,7 @@ def main():
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-local", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="seconds of untimed steps before the warmup steps (clock ramp-up)")
@@ -322,6 +323,40 @@ def main():
         local = {"workload": f"causal sliding window W={window}, B4 H16 S4096 D128 bf16", "window": window,
                  "ms": round(lms, 4), "tflops": round(lfl / (lms * 1e-3) / 1e12, 2), "flops": lfl}
 
+    # split-KV decode step: one query per head of the GQA workload shape against a
+    # 32768-key cache (attn_fwd_splitkv_bf16); bound by the K/V read
+    decode = None
+    if not args.no_decode:
+        dB, dHq, dHkv, dSkv = 8, 32, 8, 32768
+        gd = torch.Generator(device=dev)
+        gd.manual_seed(5)
+        xq = torch.randn(dB, dHq, 1, D, device=dev, generator=gd).to(torch.bfloat16)
+        xk = torch.randn(dB, dHkv, dSkv, D, device=dev, generator=gd).to(torch.bfloat16)
+        xv = torch.randn(dB, dHkv, dSkv, D, device=dev, generator=gd).to(torch.bfloat16)
+        xo = torch.empty_like(xq)
+        xl = torch.empty((dB, dHq, 1), device=dev, dtype=torch.float32)
+        nsplit = _lib.attn_splitkv_default_splits(dB, dHq, dHkv, 1, dSkv)
+        ws = torch.empty((_lib.attn_splitkv_workspace_bytes(dB, dHq, 1, D, nsplit) // 4,), device=dev,
+                         dtype=torch.float32)
+
+        def dec():
+            rc = _lib.attn_fwd_splitkv_bf16(xq.data_ptr(), xk.data_ptr(), xv.data_ptr(), xo.data_ptr(), xl.data_ptr(),
+                                            ws.data_ptr(), dB, dHq, dHkv, 1, dSkv, D, sc, 1, nsplit, sp)
+            if rc:
+                raise _lib.AttnError(rc, "attn_fwd_splitkv_bf16")
+
+        dec()
+        torch.cuda.synchronize()
+        dms = float(np.median(time_launches(dec, 20, stream)))
+        dbytes = 2 * dB * dHkv * dSkv * D * 2 + 2 * dB * dHq * D * 2 + dB * dHq * 4
+        gbs_d = dbytes / (dms * 1e-3) / 1e9
+        decode = {"workload": f"decode: B{dB} Hq{dHq} Hkv{dHkv} Sq1 Skv{dSkv} D128 bf16, split-KV (2 launches)",
+                  "nsplit": nsplit, "us": round(dms * 1e3, 2), "bytes": dbytes,
+                  "data": "torch.randn (generator seed 5) rounded to bf16",
+                  "roofline": {"bound": "hbm", "achieved": round(gbs_d, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(gbs_d / PEAK_HBM_GBS, 4)}}
+        del xq, xk, xv, xo, xl, ws
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(q, k, v, B, Hq, S, D, sc, seconds=args.cpu_seconds)
@@ -350,6 +385,7 @@ def main():
         "unfused": unfused,
         "backward": bwd,
         "local": local,
+        "decode": decode,
         "gpu": props.name,
         "cus": props.multi_processor_count,
         "timed_wall_s": round(wall, 4),
