@@ -18,6 +18,8 @@ profiling; each function's C counterpart states the definition it writes out):
   the ai-manual.ru tutorial names as the reason for custom kernels.
 * ``attn_fwd_kv`` -- Sq queries against Skv >= Sq keys and values, the
   queries being the last Sq positions (a decode step; the split-KV path).
+* ``attn_spread`` -- the spread of v around out under the attention weights
+  (no output of the method: the ingredient of the fp8 path's error bound).
 * ``qk_scores``  -- step 1 of that pipeline (q k^T, unscaled).
 * ``masked_softmax`` -- steps 2-4 (scale, mask with -inf, softmax).
 * ``pv``         -- step 5 (attn v).
@@ -83,6 +85,10 @@ class Oracle:
         L.oracle_attn_fwd_kv_rows.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64,
                                               ctypes.c_double, ctypes.c_int, _ptr, _i64, _ptr, _ptr,
                                               ctypes.c_int]
+        L.oracle_attn_fwd_spread_rows.restype = ctypes.c_int
+        L.oracle_attn_fwd_spread_rows.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64,
+                                                  ctypes.c_double, ctypes.c_int, _ptr, _i64, _ptr, _ptr,
+                                                  ctypes.c_int]
         L.oracle_qk_scores_rows.restype = ctypes.c_int
         L.oracle_qk_scores_rows.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _ptr, _i64,
                                             _ptr, ctypes.c_int]
@@ -190,6 +196,25 @@ class Oracle:
         if rows is None:
             return out.reshape(B, Hq, Sq, D), lse.reshape(B, Hq, Sq)
         return out, lse
+
+    def attn_spread(self, q, k, v, scale: float, causal: bool, rows=None, nthreads=None):
+        """Spread of v around out, per (row, d): sw = sum_j p_j |v_j - out| / l
+        and su = sum_j |v_j - out| / l with p_j = exp(s_j - max s), l = sum p_j.
+        Bounds how far out moves when the weights are rounded (fp8 path)."""
+        q, k, v = self._f32(q), self._f32(k), self._f32(v)
+        B, Hq, S, D = q.shape
+        Hkv = k.shape[1]
+        r = self._rows(rows, B * Hq * S)
+        sw = np.empty((r.size, D), dtype=np.float64)
+        su = np.empty((r.size, D), dtype=np.float64)
+        rc = self.lib.oracle_attn_fwd_spread_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                                  B, Hq, Hkv, S, D, float(scale), int(bool(causal)),
+                                                  r.ctypes.data, r.size, sw.ctypes.data, su.ctypes.data,
+                                                  self._threads(nthreads))
+        self._check(rc, "oracle_attn_fwd_spread_rows")
+        if rows is None:
+            return sw.reshape(B, Hq, S, D), su.reshape(B, Hq, S, D)
+        return sw, su
 
     # -- unfused steps ------------------------------------------------------
     def qk_scores(self, q, k, rows=None, nthreads=None):

@@ -313,6 +313,85 @@ int oracle_attn_fwd_local_rows(const float* q, const float* k, const float* v,
 }
 
 /* ------------------------------------------------------------------------ */
+/* spread of v around out (ingredient of the fp8 error bound)                */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const float *q, *k, *v;
+    shape_t sh;
+    double scale;
+    int causal;
+    const int64_t* rows;
+    double *sw, *su;
+} spread_ctx;
+
+/*
+ * With p_j = exp(s_j - m) (so max p = 1), l = sum p_j and out = sum p_j v_j / l
+ * as in attn_row:
+ *   sw_d = sum_j p_j |v_jd - out_d| / l      (weighted spread)
+ *   su_d = sum_j     |v_jd - out_d| / l      (unweighted spread)
+ * If every weight p_j is perturbed to p_j (1 + e_j) + a_j, the weighted mean
+ * moves by sum_j (p_j e_j + a_j)(v_jd - out_d) / sum_j p'_j, so
+ * |out' - out| <= (max|e| sw + max|a| su) / (1 - max|e| - S max|a| / l).
+ */
+static void spread_row(void* vctx, int64_t n, double* s) {
+    const spread_ctx* c = (const spread_ctx*)vctx;
+    const shape_t* sh = &c->sh;
+    int64_t b, h, i;
+    split_row(sh, c->rows[n], &b, &h, &i);
+    const int64_t g = kv_head(sh, h);
+    const int64_t S = sh->S, D = sh->D;
+    const float* qi = c->q + ((b * sh->Hq + h) * S + i) * D;
+    const float* kb = c->k + (b * sh->Hkv + g) * S * D;
+    const float* vb = c->v + (b * sh->Hkv + g) * S * D;
+    const int64_t jl = last_key(sh, i, c->causal);
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= jl; ++j) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += (double)qi[d] * (double)kb[j * D + d];
+        s[j] = c->scale * dot;
+        if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j <= jl; ++j) {
+        s[j] = exp(s[j] - m);
+        l += s[j];
+    }
+    for (int64_t d = 0; d < D; ++d) {
+        double o = 0.0;
+        for (int64_t j = 0; j <= jl; ++j) o += s[j] * (double)vb[j * D + d];
+        o /= l;
+        double sw = 0.0, su = 0.0;
+        for (int64_t j = 0; j <= jl; ++j) {
+            const double dv = fabs((double)vb[j * D + d] - o);
+            sw += s[j] * dv;
+            su += dv;
+        }
+        c->sw[n * D + d] = sw / l;
+        c->su[n * D + d] = su / l;
+    }
+}
+
+int oracle_attn_fwd_spread_rows(const float* q, const float* k, const float* v,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t S, int64_t D,
+                                double scale, int causal, const int64_t* rows, int64_t nrows,
+                                double* sw, double* su, int nthreads) {
+    spread_ctx c;
+    c.q = q; c.k = k; c.v = v;
+    c.sh.B = B; c.sh.Hq = Hq; c.sh.Hkv = Hkv; c.sh.S = S; c.sh.D = D;
+    c.scale = scale;
+    c.causal = causal ? 1 : 0;
+    c.rows = rows;
+    c.sw = sw;
+    c.su = su;
+    int rc = check_shape(&c.sh);
+    if (rc) return rc;
+    rc = check_rows(&c.sh, rows, nrows);
+    if (rc) return rc;
+    return run_rows(spread_row, &c, nrows, S, nthreads);
+}
+
+/* ------------------------------------------------------------------------ */
 /* queries against a longer key/value sequence (decode, split-KV)            */
 /* ------------------------------------------------------------------------ */
 

@@ -11,6 +11,8 @@ PCG64 (``default_rng(seed).standard_normal(dtype=float32)``), drawn in the
 order q, k, v, then rounded to bfloat16 with round-to-nearest-even when the
 config is bf16.  The oracle and the GPU see bit-identical values: the oracle
 gets the float32 image of each bf16 value (exact), the GPU gets the bf16 bits.
+For the fp8 path the same draws are quantised to e4m3fn codes with one
+power-of-two scale per tensor; the oracle gets code value x scale (exact).
 """
 from __future__ import annotations
 
@@ -74,6 +76,79 @@ def make_dout(B: int, Hq: int, S: int, D: int, dtype: str, seed: int) -> Tensor:
     same seed are unchanged."""
     rng = np.random.default_rng([seed, 1])
     return _finish(rng.standard_normal((B, Hq, S, D), dtype=np.float32), dtype)
+
+
+# ---------------------------------------------------------------------------
+# fp8 (OCP E4M3, "e4m3fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; no
+# infinities; exponent 15 with mantissa 7 is NaN, so the largest finite value
+# is 448; exponent 0 holds subnormals m/8 * 2^-6.
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """float32 value of e4m3fn codes (uint8); NaN for the two NaN codes."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return (sign * val).astype(np.float32)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest e4m3fn code, ties to even, clamping
+    to +-448 first (inputs are finite)."""
+    x = np.clip(np.asarray(x, dtype=np.float64), -E4M3_MAX, E4M3_MAX)
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.int64)
+    a = np.abs(x)
+    # grid spacing at |x|: 2^(e-3) in the normal range e >= -6, 2^-9 below
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6)
+    step = 2.0 ** (e - 3)
+    q = a / step
+    r = np.floor(q)
+    frac = q - r
+    r = r + ((frac > 0.5) | ((frac == 0.5) & (r % 2 == 1)))  # nearest, ties to even multiple
+    mag = r * step  # exact multiple of the grid (may step up to the next binade)
+    # encode the magnitude: subnormal if < 2^-6
+    ee = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
+    sub = mag < 2.0 ** -6
+    code_sub = np.round(mag / 2.0 ** -9).astype(np.int64)
+    mant = np.round((mag / 2.0 ** ee - 1.0) * 8).astype(np.int64)
+    code_norm = ((ee + 7).astype(np.int64) << 3) | mant
+    code = np.where(sub, code_sub, code_norm)
+    return (sign | code).astype(np.uint8)
+
+
+@dataclass
+class Fp8Tensor:
+    """e4m3fn codes with a per-tensor scale: value = decode(code) * scale.
+    ``f32`` is that value (exact in float32: the scale is a power of two)."""
+
+    codes: np.ndarray
+    scale: float
+    f32: np.ndarray
+
+
+def to_fp8(x32: np.ndarray) -> Fp8Tensor:
+    """Per-tensor power-of-two scale that maps max |x| inside +-448, then
+    round-to-nearest-even to e4m3fn."""
+    amax = float(np.max(np.abs(x32))) if x32.size else 0.0
+    scale = 2.0 ** int(np.ceil(np.log2(amax / E4M3_MAX))) if amax > 0 else 1.0
+    codes = e4m3_encode(np.asarray(x32, np.float64) / scale)
+    return Fp8Tensor(codes=codes, scale=scale, f32=(e4m3_decode(codes).astype(np.float64) * scale).astype(np.float32))
+
+
+def make_qkv_fp8(B: int, Hq: int, Hkv: int, S: int, D: int, seed: int):
+    """The same N(0,1) draws as make_qkv (same seed), quantised to e4m3fn
+    with one power-of-two scale per tensor."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, S, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    return to_fp8(q), to_fp8(k), to_fp8(v)
 
 
 def make_scores(B: int, H: int, S: int, D: int, seed: int) -> np.ndarray:

@@ -30,6 +30,8 @@ What pins what:
     equals the square forward, each query row equals the square causal
     forward's row at its position, and torch's float64 SDPA with an explicit
     bottom-right mask.
+  spread of v around out (fp8 error bound ingredient): the S = 2 closed form,
+    zero for one key and for constant v.
   backward (chain-rule derivative of the forward; the ai-manual.ru tutorial,
   section 6, only warns that the flash backward is easy to get wrong):
     central finite differences of sum(dout * out) through the pinned forward
@@ -533,6 +535,45 @@ KV_PINS = [pin_kv_square, pin_kv_suffix_rows, pin_kv_torch]
 
 
 # --------------------------------------------------------------------------
+# spread of v around out (fp8 error bound)
+# --------------------------------------------------------------------------
+
+def pin_spread_closed_forms(orc):
+    """S = 2: with weights w0, w1 = 1 - w0, sw = 2 w0 w1 |v0 - v1| and
+    su = (|v0 - out| + |v1 - out|) / l, l = 1 + exp(-|s0 - s1|).  S = 1 and a
+    constant v give zero spread."""
+    q = np.array([[[[1.0, 0.5]]] * 1], np.float32).reshape(1, 1, 1, 2)
+    q = np.concatenate([q, q], axis=2)  # two identical queries
+    k = np.array([[[[0.5, 1.0], [1.5, -0.5]]]], np.float32)
+    v = np.array([[[[2.0, -1.0], [0.5, 3.0]]]], np.float32)
+    sc = 0.7
+    sw, su = orc.attn_spread(q, k, v, sc, False)
+    s0 = sc * (1.0 * 0.5 + 0.5 * 1.0)
+    s1 = sc * (1.0 * 1.5 + 0.5 * -0.5)
+    w0 = 1 / (1 + math.exp(s1 - s0))
+    w1 = 1 - w0
+    out = w0 * v[0, 0, 0].astype(np.float64) + w1 * v[0, 0, 1].astype(np.float64)
+    l = 1 + math.exp(-abs(s0 - s1))
+    exp_sw = 2 * w0 * w1 * np.abs(v[0, 0, 0] - v[0, 0, 1]).astype(np.float64)
+    exp_su = (np.abs(v[0, 0, 0] - out) + np.abs(v[0, 0, 1] - out)) / l
+    _close(sw[0, 0, 1], exp_sw, 1e-14, "spread S=2 sw")
+    _close(su[0, 0, 1], exp_su, 1e-14, "spread S=2 su")
+    swc, suc = orc.attn_spread(q, k, v, sc, True)
+    _close(swc[0, 0, 0], np.zeros(2), 0.0, "spread causal row 0 (one key) sw")
+    _close(suc[0, 0, 0], np.zeros(2), 0.0, "spread causal row 0 (one key) su")
+    _close(swc[0, 0, 1], exp_sw, 1e-14, "spread causal row 1 = full row 1")
+    qq = _randn((1, 2, 9, 4), 130)
+    kk = _randn((1, 2, 9, 4), 131)
+    vv = np.ones((1, 2, 9, 4), np.float32) * np.float32(1.5)
+    sw, su = orc.attn_spread(qq, kk, vv, 0.5, True)
+    _close(sw, np.zeros_like(sw), 1e-15, "constant v sw")
+    _close(su, np.zeros_like(su), 1e-15, "constant v su")
+
+
+SPREAD_PINS = [pin_spread_closed_forms]
+
+
+# --------------------------------------------------------------------------
 # backward
 # --------------------------------------------------------------------------
 
@@ -649,4 +690,4 @@ def pin_bwd_special(orc):
 
 BWD_PINS = [pin_bwd_finite_diff, pin_bwd_torch, pin_bwd_invariants, pin_bwd_special]
 
-ALL_PINS = ATTN_PINS + STEP_PINS + LOCAL_PINS + KV_PINS + BWD_PINS
+ALL_PINS = ATTN_PINS + STEP_PINS + LOCAL_PINS + KV_PINS + SPREAD_PINS + BWD_PINS
