@@ -97,6 +97,24 @@ attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* 
                          void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Fused forward with fp8 operands (OCP E4M3, "e4m3fn").
+ *
+ * q [B,Hq,S,D], k and v [B,Hkv,S,D]: one byte per element, e4m3fn codes;
+ * the value of an element is decode(code) * q_scale (k_scale, v_scale), one
+ * float scale per tensor.  out: bfloat16 [B,Hq,S,D]; lse: float32 [B,Hq,S] or
+ * NULL.  Computes the same attention as attn_fwd_bf16 on those values, with
+ * the products on the fp8 matrix cores (twice the bf16 rate): q k^T exactly
+ * (fp8 products, float32 sums), the probabilities rounded to e4m3 (as p * 2^8)
+ * for the product with v, and out normalised by the sum of the rounded
+ * probabilities.  The ai-manual.ru tutorial (section 6) names FP8 as the next
+ * factor of two after bf16.  scale, q_scale, k_scale, v_scale: finite, > 0.
+ * One kernel launch, no workspace.
+ * ------------------------------------------------------------------------- */
+attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int B, int Hq, int Hkv, int S, int D, float scale, float q_scale, float k_scale,
+                         float v_scale, int causal, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Fused forward with a causal sliding window (bfloat16).
  *
  * As attn_fwd_bf16 with causal = 1, except that query i sees only keys

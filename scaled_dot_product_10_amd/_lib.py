@@ -32,6 +32,7 @@ _f = ctypes.c_float
 SIGNATURES = {
     "attn_fwd_bf16": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "attn_fwd_f32": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
+    "attn_fwd_fp8": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _f, _f, _f, _i, _p]),
     "attn_fwd_local_bf16": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "attn_qk_gemm_bf16": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "attn_qk_gemm_f32": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p]),
@@ -89,6 +90,11 @@ def attn_fwd_bf16(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, stream) ->
 
 def attn_fwd_f32(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, stream) -> int:
     return _call("attn_fwd_f32", q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, stream)
+
+
+def attn_fwd_fp8(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, q_scale, k_scale, v_scale, causal, stream) -> int:
+    return _call("attn_fwd_fp8", q, k, v, out, lse, B, Hq, Hkv, S, D, scale, q_scale, k_scale, v_scale, causal,
+                 stream)
 
 
 def attn_fwd_local_bf16(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, window, stream) -> int:

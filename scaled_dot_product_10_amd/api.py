@@ -225,3 +225,36 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
                                       _stream(q.device))
     _raise(code, "attn_fwd_splitkv_bf16")
     return out, lse
+
+
+def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_scale: float, k_scale: float, v_scale: float, *,
+            causal: bool = True, scale: float | None = None, out: torch.Tensor | None = None,
+            lse: torch.Tensor | bool | None = True):
+    """fp8 forward: q ``[B,Hq,S,D]``, k/v ``[B,Hkv,S,D]`` hold e4m3fn codes
+    (``torch.uint8`` or ``torch.float8_e4m3fn``) with per-tensor scales.
+    Returns ``(out, lse)``; out is bf16."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{n} must hold e4m3fn codes (uint8 or float8_e4m3fn), got {t.dtype}")
+        _check(t, n)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, S, D) or tuple(v.shape) != (B, Hkv, S, D):
+        raise ValueError(f"k/v shapes {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, S, D), device=q.device, dtype=torch.bfloat16)
+    else:
+        _check(out, "out", torch.bfloat16)
+    if lse is True:
+        lse = torch.empty((B, Hq, S), device=q.device, dtype=torch.float32)
+    elif lse is False:
+        lse = None
+    elif lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+    code = _lib.attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr() if lse is not None else None, B, Hq, Hkv, S, D, float(scale),
+                             float(q_scale), float(k_scale), float(v_scale), int(bool(causal)), _stream(q.device))
+    _raise(code, "attn_fwd_fp8")
+    return out, lse

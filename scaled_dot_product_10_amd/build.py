@@ -21,7 +21,7 @@ INCLUDE = ROOT / "include"
 BUILD = ROOT / "_build"
 LIB = PKG / "libattn.so"
 
-SOURCES = ["attn_api.hip", "fwd_bf16.hip", "fwd_f32.hip", "unfused.hip", "bwd_bf16.hip", "splitkv_bf16.hip"]
+SOURCES = ["attn_api.hip", "fwd_bf16.hip", "fwd_f32.hip", "unfused.hip", "bwd_bf16.hip", "splitkv_bf16.hip", "fwd_fp8.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

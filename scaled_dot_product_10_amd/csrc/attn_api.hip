@@ -188,6 +188,46 @@ attn_status attn_fwd_local_bf16(const void* q, const void* k, const void* v, voi
     return hip_status(attn::launch_fwd_bf16(a, (hipStream_t)stream));
 }
 
+attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
+                         int S, int D, float scale, float q_scale, float k_scale, float v_scale, int causal,
+                         void* stream) {
+    if (!q || !k || !v || !out) return ATTN_ERR_NULL_POINTER;
+    if (bad_dims(B, Hq, Hkv, S)) return ATTN_ERR_BAD_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return ATTN_ERR_UNSUPPORTED;
+    for (float x : {scale, q_scale, k_scale, v_scale})
+        if (!isfinite(x) || !(x > 0.f)) return ATTN_ERR_BAD_SCALE;
+    if (!isfinite(scale * q_scale * k_scale * 1.4426950408889634f)) return ATTN_ERR_BAD_SCALE;
+    const int64_t nq8 = prod({B, Hq, S, D});
+    const int64_t nkv8 = prod({B, Hkv, S, D});
+    const int64_t no = prod({B, Hq, S, D, 2});
+    const int64_t nl = prod({B, Hq, S, 4});
+    if (nq8 < 0 || nkv8 < 0 || no < 0 || nl < 0) return ATTN_ERR_BAD_SHAPE;
+    if (prod({B, Hq, (S + 127) / 128}) > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) || misaligned(lse, 4))
+        return ATTN_ERR_MISALIGNED;
+    if (overlap(out, no, q, nq8) || overlap(out, no, k, nkv8) || overlap(out, no, v, nkv8) ||
+        overlap(lse, nl, q, nq8) || overlap(lse, nl, k, nkv8) || overlap(lse, nl, v, nkv8) || overlap(lse, nl, out, no))
+        return ATTN_ERR_ALIAS;
+    attn::Fp8Args a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.S = S;
+    a.D = D;
+    a.scale = scale;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.causal = causal;
+    return hip_status(attn::launch_fwd_fp8(a, (hipStream_t)stream));
+}
+
 attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse, int B, int Hq,
                          int Hkv, int S, int D, float scale, int causal, void* stream) {
     const attn_status st = check_fwd(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, 4);

@@ -58,6 +58,17 @@ struct BwdArgs {
     int causal;
 };
 
+struct Fp8Args {
+    const void* q;  // e4m3 codes [B, Hq, S, D]
+    const void* k;  // e4m3 codes [B, Hkv, S, D]
+    const void* v;
+    void* out;      // bf16 [B, Hq, S, D]
+    float* lse;     // may be null
+    int B, Hq, Hkv, S, D;
+    float scale, q_scale, k_scale, v_scale;
+    int causal;
+};
+
 struct SplitKvArgs {
     const void* q;     // [B, Hq, Sq, D]
     const void* k;     // [B, Hkv, Skv, D]
@@ -73,6 +84,7 @@ struct SplitKvArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 hipError_t launch_qk_gemm_bf16(const QkArgs& a, hipStream_t stream);
 hipError_t launch_qk_gemm_f32(const QkArgs& a, hipStream_t stream);
 hipError_t launch_masked_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream);

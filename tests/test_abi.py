@@ -40,7 +40,7 @@ def L():
 
 def test_header_symbols_are_exported(L):
     syms = header_symbols()
-    assert len(syms) == 18, syms
+    assert len(syms) == 19, syms
     nm = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)], capture_output=True, text=True,
                         check=True).stdout
     exported = set(re.findall(r"\bT (\w+)$", nm, flags=re.M))
@@ -101,6 +101,28 @@ def fwd_args(**kw):
 ])
 def test_fwd_rejects(fn, kw, code):
     assert fn(*fwd_args(**kw)) == code
+
+
+def test_fp8_rejects():
+    f = _lib.attn_fwd_fp8
+    base = dict(q=A, k=Bp, v=C, out=Dp, lse=E, B=1, Hq=2, Hkv=1, S=16, D=128, scale=0.1, qs=0.01, ks=0.01, vs=0.01,
+                causal=1, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return f(*[a[n] for n in ("q", "k", "v", "out", "lse", "B", "Hq", "Hkv", "S", "D", "scale", "qs", "ks", "vs",
+                                  "causal", "stream")])
+
+    assert call(q=None) == NULL
+    assert call(Hq=3, Hkv=2) == SHAPE
+    assert call(D=96) == UNSUP
+    assert call(qs=0.0) == SCALE
+    assert call(vs=float("inf")) == SCALE
+    assert call(scale=1e30, qs=1e30) == SCALE
+    assert call(k=Bp + 8) == ALIGN
+    assert call(out=Bp) == ALIAS
+    assert call(lse=Dp + 64) == ALIAS
 
 
 def test_local_rejects():
