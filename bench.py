@@ -32,6 +32,7 @@ sys.path.insert(0, str(ROOT))
 METRIC = "fused causal attn fwd TFLOP/s + % bf16 MFMA peak (B4 H16 S4096 D128)"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA (twice the bf16 rate)
 PROFILE = ROOT / "profiles" / "fwd_bf16_B4H16S4096D128_causal.md"
 KERNEL_SOURCES = ["fwd_bf16.hip", "common.h"]
 
@@ -134,6 +135,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-local", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="seconds of untimed steps before the warmup steps (clock ramp-up)")
@@ -323,6 +325,33 @@ def main():
         local = {"workload": f"causal sliding window W={window}, B4 H16 S4096 D128 bf16", "window": window,
                  "ms": round(lms, 4), "tflops": round(lfl / (lms * 1e-3) / 1e12, 2), "flops": lfl}
 
+    # fp8 forward on the same shape: N(0,1) draws in e4m3fn with one power-of-two
+    # scale per tensor (2^-6 keeps max |x| < 448 * 2^-6 = 7)
+    fp8 = None
+    if not args.no_fp8:
+        g8 = torch.Generator(device=dev)
+        g8.manual_seed(3)
+        s8 = 2.0 ** -6
+        q8, k8, v8 = [(torch.randn(B, h_, S, D, device=dev, generator=g8) / s8).to(torch.float8_e4m3fn)
+                      for h_ in (Hq, Hkv, Hkv)]
+        o8 = torch.empty_like(dq)
+
+        def fwd8():
+            rc = _lib.attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o8.data_ptr(), lse.data_ptr(),
+                                   B, Hq, Hkv, S, D, sc, s8, s8, s8, 1, sp)
+            if rc:
+                raise _lib.AttnError(rc, "attn_fwd_fp8")
+
+        fwd8()
+        torch.cuda.synchronize()
+        f8ms = float(np.median(time_launches(fwd8, 20, stream)))
+        f8tf = attn_flops(B, Hq, S, D, True) / (f8ms * 1e-3) / 1e12
+        fp8 = {"workload": "causal attention forward B4 H16 S4096 D128, e4m3fn q/k/v, bf16 out",
+               "data": "torch.randn (generator seed 3) / 2^-6 rounded to e4m3fn",
+               "ms": round(f8ms, 4), "tflops": round(f8tf, 2),
+               "frac_fp8_peak": round(f8tf / PEAK_FP8_TFLOPS, 4), "peak_fp8_tflops": PEAK_FP8_TFLOPS}
+        del q8, k8, v8, o8
+
     # split-KV decode step: one query per head of the GQA workload shape against a
     # 32768-key cache (attn_fwd_splitkv_bf16); bound by the K/V read
     decode = None
@@ -386,6 +415,7 @@ def main():
         "backward": bwd,
         "local": local,
         "decode": decode,
+        "fp8": fp8,
         "gpu": props.name,
         "cus": props.multi_processor_count,
         "timed_wall_s": round(wall, 4),
