@@ -7,30 +7,36 @@
 // in FP8 for about another 2x) is the idea; v_mfma_scale_f32_32x32x64_f8f6f4
 // (unit block scales) does 32x32x64 per instruction, twice the bf16 rate.
 //
-// Layout and schedule: 128 queries per workgroup (32 per wave), 64-key tiles
-// of K and V through LDS (whole-row loads, the next tile in registers while
-// the current one is multiplied).  Per tile and wave:
-//   S^T = K.Q^T: A = K rows from LDS (32 bytes of d per lane), B = Q (kept in
-//     registers); two 32-key blocks.
-//   softmax: exact running max per query (so every p <= 1), p scaled by 2^8
-//     (so the small ones stay in e4m3's normal range) and rounded to e4m3;
-//     the sum l adds the rounded values back, so out is an exact convex
-//     combination of v rows under the weights actually used.
-//   O^T += V^T.P^T: A = V^T via ds_read_b64_tr_b8, B = the 32 e4m3 weights a
-//     lane holds (its two 16-key halves of the S^T accumulators).
+// The schedule is the bf16 kernel's (fwd_bf16.hip): 8 waves, 256 queries per
+// workgroup (32 per wave), 64-key tiles of K and V brought into LDS by
+// global_load_lds_dwordx4 and double-buffered, and two wave groups one phase
+// apart, so on every SIMD one wave runs the matrix products of a tile while
+// its partner runs the softmax of the next:
+//   M phase:  S(n+1)^T = K(n+1).Q^T (A = K rows from LDS, 32 bytes of d per
+//             lane; B = Q in registers), O^T += V(n)^T.P(n)^T (A = V^T through
+//             ds_read_b64_tr_b8; B = the 32 e4m3 weights a lane holds), and
+//             one more product of an all-ones A with P(n)^T whose every row is
+//             the tile's sum of the rounded weights (the row sum l, without a
+//             vector-ALU decode of the e4m3 bytes).
+//   V phase:  mask, then p * 2^8 = 2^(s c - m + 8) rounded to e4m3.  The
+//             reference m is only raised when some score of the tile exceeds
+//             it by more than 2^0.75, which keeps every stored value below
+//             2^8.75 < 448 (the largest e4m3 value) and makes the rescaling
+//             of O and l rare.  The first tile always sets it.
 // The k order of an fp8 product only has to agree between A and B within each
-// half-wave; the transposed V reads are arranged to match the accumulator's
-// key order (rows 8(r/4) + 4g + r%4 of each 32-key block).
+// half-wave; the transposed V reads give each lane the keys of the S^T
+// accumulator rows (8(r/4) + 4g + r%4 of each 32-key block) in that order.
 #include "common.h"
 #include "launch.h"
 
 namespace attn {
 namespace {
 
-constexpr int NT = 256;  // 4 waves
-constexpr int BM = 128;  // queries per workgroup
+constexpr int BM = 256;  // queries per workgroup
 constexpr int BN = 64;   // keys per tile
-constexpr float kPScale = 256.0f;  // p in (0, 1] is stored as p * 2^8 (<= 256 < 448)
+constexpr int NW = 8;    // waves (two per SIMD)
+constexpr int NT = NW * 64;
+constexpr float kSlack = 0.75f;  // stored p * 2^8 <= 2^(8 + kSlack) < 448
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
@@ -44,69 +50,135 @@ struct Fp8Params {
     float* lse;
     int Hq, Hkv, S, group, nq;
     uint32_t total;
-    float c;      // softmax scale * q_scale * k_scale * log2(e)
-    float vs;     // v_scale
+    uint32_t hgrp;  // causal: heads whose tiles one XCD runs together (0: plain order)
+    float c;        // softmax scale * q_scale * k_scale * log2(e)
+    float vs;       // v_scale
 };
+
+constexpr int kSlotsPerXcd = 32;  // 32 CUs per XCD, one workgroup per CU
 
 // 32x32x64 e4m3 x e4m3 -> f32 (block scales 2^0)
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// LDS tile: rows x D bytes, 16-byte chunks; chunk c of row r at c ^ swz(r).
+// LDS tile: BN rows x D bytes, 16-byte chunks; chunk c of row r at c ^ swz(r).
 // Row reads (16 lanes on 16 rows) and the transposed byte reads (16 lanes on
-// 8 rows) both hit distinct banks.
+// 8 rows, 16 bytes each) both hit distinct banks.
 template <int D>
-struct Fp8Tile {
-    static constexpr int CPR = D / 16;  // chunks per row
+struct Tile8 {
+    static constexpr int CPR = D / 16;
+    static constexpr int BYTES = BN * D;           // 8 KB (D=128) / 4 KB (D=64)
+    static constexpr int CHUNKS = BYTES / 1024;    // DMA instructions per tile
+    static_assert(CHUNKS >= 1 && CHUNKS <= NW, "one DMA instruction per wave at most");
     __device__ static int swz(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
     __device__ static int at(int r, int chunk) { return r * D + ((chunk ^ swz(r)) << 4); }
 };
 
-// BN rows [r0, r0 + BN) of a [S, D] byte matrix -> registers -> LDS; rows past S are zero
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One global_load_lds_dwordx4: 64 lanes x 16 bytes into 1 KB of LDS at lds
+// (wave-uniform), lane L filling bytes [16L, 16L+16) from base + off.  Inline
+// assembly so later LDS reads are not ordered after it; completion is awaited
+// with s_waitcnt vmcnt(0) before the barrier that publishes the tile.  M0 is
+// reserved and reloaded by the compiler before each of its own uses.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory");
+}
+
+// DMA of one K or V tile: wave w (< CHUNKS) fills LDS positions
+// p = 64 w + lane, i.e. row p / CPR at chunk position p % CPR, which holds
+// chunk (p % CPR) ^ swz(row); rows past the sequence repeat row S-1 (their
+// keys are masked).
 template <int D>
-struct Fp8Rows {
-    static constexpr int CPR = D / 16;
-    static constexpr int CH = BN * CPR / NT;
-    static_assert(CH >= 1 && CH * NT == BN * CPR, "tile/thread mismatch");
-    u32x4 r[CH];
-    __device__ __forceinline__ void load(const uint8_t* base, int r0, int S, int tid) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + NT * i, row = r0 + c / CPR;
-            r[i] = row < S ? *(const u32x4*)(base + (int64_t)row * D + (c % CPR) * 16) : u32x4{0, 0, 0, 0};
-        }
+struct DmaPlan8 {
+    using T = Tile8<D>;
+    uint32_t off;
+    __device__ __forceinline__ void init(int wave, int lane) {
+        const int pos = wave * 64 + lane;
+        const int r = pos / T::CPR;
+        off = (uint32_t)(r * D + (((pos % T::CPR) ^ T::swz(r)) << 4));
     }
-    __device__ __forceinline__ void store(uint8_t* t, int tid) const {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + NT * i;
-            *(u32x4*)(t + Fp8Tile<D>::at(c / CPR, c % CPR)) = r[i];
+    __device__ __forceinline__ void issue(const uint8_t* base, int n0, int S, uint8_t* tile, int wave) const {
+        if (wave >= T::CHUNKS) return;
+        const uint8_t* tb = base + (int64_t)n0 * D;
+        const uint32_t l0 = lds_addr(tile) + (uint32_t)wave * 1024u;
+        if (n0 + BN <= S) {
+            dma16(tb, off, l0);
+        } else {
+            const int r = (int)(off / D);
+            const int last = S - 1 - n0;
+            dma16(tb, off - (uint32_t)((r - min(r, last)) * D), l0);
         }
     }
 };
 
+// Workgroup barrier between phases (see fwd_bf16.hip): LDS reads drained
+// first, with wait_dma this wave's tile DMA as well; no compiler fence.
+__device__ __forceinline__ void phase_barrier(bool wait_dma) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (wait_dma)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(Fp8Params p) {
+__global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Params p) {
+    using T = Tile8<D>;
     constexpr int KS = D / 64;  // k-steps of the Q.K^T product
     constexpr int DB = D / 32;  // 32-row blocks of O^T
-    using T = Fp8Tile<D>;
-    __shared__ __attribute__((aligned(16))) uint8_t Ks[BN * D];
-    __shared__ __attribute__((aligned(16))) uint8_t Vs[BN * D];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * T::BYTES];
+    auto Kbuf = [&](int i) __attribute__((always_inline)) { return smem + (i & 1) * T::BYTES; };
+    auto Vbuf = [&](int i) __attribute__((always_inline)) { return smem + (2 + (i & 1)) * T::BYTES; };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, g = lane >> 5;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+
     const uint32_t L = xcd_remap(blockIdx.x, p.total);
-    const int bh = (int)(L / (uint32_t)p.nq);
-    const int tile = CAUSAL ? p.nq - 1 - (int)(L % (uint32_t)p.nq) : (int)(L % (uint32_t)p.nq);
+    int bh, tile;
+    if (CAUSAL) {
+        if (p.hgrp > 0 && blockIdx.x < p.total / 8u * 8u) {
+            // groups of hgrp heads fill one XCD, longest tiles first (as in the bf16 kernel)
+            const uint32_t per = p.total / 8u;
+            const uint32_t loc = L % per;
+            const uint32_t gsz = p.hgrp * (uint32_t)p.nq;
+            const uint32_t r = loc % gsz;
+            tile = p.nq - 1 - (int)(r / p.hgrp);
+            bh = (int)((L - loc) / (uint32_t)p.nq + (loc / gsz) * p.hgrp + r % p.hgrp);
+        } else {
+            bh = (int)(L / (uint32_t)p.nq);
+            tile = p.nq - 1 - (int)(L % (uint32_t)p.nq);
+        }
+    } else {
+        bh = (int)(L / (uint32_t)p.nq);
+        tile = (int)(L % (uint32_t)p.nq);
+    }
     const int b = bh / p.Hq, h = bh % p.Hq, kvh = h / p.group;
     const int S = p.S;
     const int m0 = tile * BM;
-    const int qw = m0 + wave * 32;
-    const int qi = qw + l32;
     const int64_t row0 = (int64_t)bh * S;
     const uint8_t* kb = p.k + ((int64_t)b * p.Hkv + kvh) * S * D;
     const uint8_t* vb = p.v + ((int64_t)b * p.Hkv + kvh) * S * D;
+    const int qwmin = m0 + wave * 32;
+    const int qwmax = qwmin + 31;
+    const int qi = qwmin + l32;
+    const int qlast = min(m0 + BM, S) - 1;
+    const int ntiles = (S + BN - 1) / BN;
+    const int nend = CAUSAL ? min(ntiles, qlast / BN + 1) : ntiles;
+
+    DmaPlan8<D> dma;
+    dma.init(wave, lane);
+    dma.issue(kb, 0, S, Kbuf(0), wave);
+    dma.issue(vb, 0, S, Vbuf(0), wave);
+    if (nend > 1) dma.issue(kb, BN, S, Kbuf(1), wave);
 
     // Q operand: query qi, d = 64 ks + 32 g .. +31
     i32x8 qreg[KS];
@@ -120,18 +192,17 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(Fp8Params p) {
         }
         qreg[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
-    // K row read of row l32 (+32 sb), chunks 4 ks + 2 g and + 1
+    // K row reads: row l32 (+32 for the second key block), chunks 4 ks + 2 g, + 1
     int koff[KS][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         koff[ks][0] = T::at(l32, 4 * ks + 2 * g);
         koff[ks][1] = T::at(l32, 4 * ks + 2 * g + 1);
     }
-    // transposed V read u (bytes 8u..8u+7 of the A operand): source lane
-    // s = lane % 16 names key row 16u + 8(t/4) + 4g + t%4 (t = s/2) and the 8
-    // bytes at d = 32 db + 16 (G%2) + 8 (s%2) of it, where G = lane / 16; the
-    // 16 lanes of G then each receive one d (32 db + 16 (G%2) + lane % 16) for
-    // the 8 keys.  Adding 16 rows leaves the swizzle unchanged.
+    // transposed V read u (A bytes 8u..8u+7): source lane s = lane % 16 names
+    // key row 16u + 8(t/4) + 4g + t%4 (t = s/2) and its 8 bytes at
+    // d = 32 db + 16 (G%2) + 8 (s%2), G = lane / 16; each lane of G then holds
+    // d = 32 db + lane % 32 for those 8 keys.  +16 rows keeps the swizzle.
     int voff[DB];
     {
         const int G = lane >> 4, s = lane & 15, t = s >> 1, par = s & 1;
@@ -139,66 +210,38 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) voff[db] = T::at(r, 2 * db + (G & 1)) + 8 * par;
     }
+    const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
     const float c = p.c;
-    float m = -INFINITY;  // running max of s * c for query qi
-    float l = 0.f;        // running sum of the rounded 2^8 p over this lane's keys
     f32x16 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    f32x16 lacc = f32x16{};  // every row: running sum of the stored p * 2^8
+    // reference max of query qi in scaled log2 units; a finite start so that
+    // no exponent argument is inf - inf; the first tile always moves it
+    float mc = -1e30f;
+    f32x16 sacc[2];
+    i32x8 pb;
 
-    const int qlast = min(m0 + BM, S) - 1;
-    const int ntiles = CAUSAL ? qlast / BN + 1 : (S + BN - 1) / BN;
-    Fp8Rows<D> tk, tv;
-    tk.load(kb, 0, S, tid);
-    tv.load(vb, 0, S, tid);
-    for (int n = 0; n < ntiles; ++n) {
-        const int n0 = n * BN;
-        __syncthreads();  // previous tile consumed
-        tk.store(Ks, tid);
-        tv.store(Vs, tid);
-        __syncthreads();
-        if (n + 1 < ntiles) {
-            tk.load(kb, n0 + BN, S, tid);
-            tv.load(vb, n0 + BN, S, tid);
-        }
-        if (CAUSAL && n0 > qw + 31) continue;  // every key after every query of the wave
-        f32x16 sacc[2];
+    // S^T = K.Q^T for the tile in Kt
+    auto qk = [&](const uint8_t* Kt) __attribute__((always_inline)) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             sacc[sb] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 a0 = *(const u32x4*)(Ks + sb * 32 * D + koff[ks][0]);
-                const u32x4 a1 = *(const u32x4*)(Ks + sb * 32 * D + koff[ks][1]);
+                const u32x4 a0 = *(const u32x4*)(Kt + sb * 32 * D + koff[ks][0]);
+                const u32x4 a1 = *(const u32x4*)(Kt + sb * 32 * D + koff[ks][1]);
                 const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
                 sacc[sb] = mfma_fp8(a, qreg[ks], sacc[sb]);
             }
         }
-        // accumulator row r of block sb: key n0 + 32 sb + 8(r/4) + 4g + r%4
-        float t = -INFINITY;
-        const bool edge = (CAUSAL && n0 + BN - 1 > qw) || n0 + BN > S;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                if (edge) {
-                    const int key = n0 + sb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if ((CAUSAL && key > qi) || key >= S) sacc[sb][r] = -INFINITY;
-                }
-                t = fmaxf(t, sacc[sb][r]);
-            }
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
-        const float mn = fmaxf(m, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c);
-        const float mref = mn == -INFINITY ? 0.f : mn;  // nothing visible yet: p = 0, nothing to rescale
-        const float alpha = fast_exp2(m - mref);
-        m = mn;
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        // p * 2^8 -> e4m3, packed in the accumulator's order (byte 16 sb + r)
-        i32x8 pb;
-        const float moff = mref - 8.0f;  // 2^(s c - m) * 2^8
+    };
+
+    // p * 2^8 = 2^(s c - mc + 8) -> e4m3, byte 16 sb + r of the B operand
+    auto exp_pack = [&](float mref) __attribute__((always_inline)) {
+        const float moff = mref - 8.0f;
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
             const int sb = w >> 2, r = (w & 3) * 4;
@@ -208,26 +251,127 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(Fp8Params p) {
             x = __builtin_amdgcn_cvt_pk_fp8_f32(fast_exp2(fmaf(sacc[sb][r + 2], c, -moff)),
                                                 fast_exp2(fmaf(sacc[sb][r + 3], c, -moff)), x, true);
             pb[w] = x;
-            l += (__builtin_amdgcn_cvt_f32_fp8(x, 0) + __builtin_amdgcn_cvt_f32_fp8(x, 1)) +
-                 (__builtin_amdgcn_cvt_f32_fp8(x, 2) + __builtin_amdgcn_cvt_f32_fp8(x, 3));
         }
+    };
+
+    // softmax of tile n0 (from sacc)
+    auto softmax = [&](int n0) __attribute__((always_inline)) {
+        if ((CAUSAL && n0 + BN - 1 > qwmin) || n0 + BN > S) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = n0 + sb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                    if ((CAUSAL && key > qi) || key >= S) sacc[sb][r] = -INFINITY;
+                }
+        }
+        float t[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t[i] = fmaxf(sacc[0][i], sacc[1][i]);
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
+        if (__builtin_amdgcn_ballot_w64(t[0] * c > mc + kSlack)) {
+            // raise the reference to the row's tile max (both half-waves of a
+            // query agree) and rescale what was accumulated against the old one
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[0]), __float_as_uint(t[0]), false, false);
+            const float mnew = fmaxf(mc, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c);
+            const float alpha = fast_exp2(mc - mnew);  // 0 on the first tile
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            lacc *= alpha;
+            mc = mnew;
+        }
+        exp_pack(mc);
+    };
+
+    auto active = [&](int n) __attribute__((always_inline)) { return !CAUSAL || n * BN <= qwmax; };
+
+    phase_barrier(true);
+
+    // M(n): S(n+1) = K(n+1).Q^T, O += P(n).V(n), l += P(n).1; operands read
+    // AHEAD products in advance.  For the last tile the S(n+1) product reads
+    // the (stale, in-bounds) other K buffer and its result is never used.
+    auto mphase = [&](int n) __attribute__((always_inline)) {
+        if (!active(n)) return;
+        constexpr int NQK = 2 * KS, NP = NQK + DB, AHEAD = 3;
+        const uint8_t* Kt = Kbuf(n + 1);
+        const uint8_t* Vt = Vbuf(n);
+        auto rd = [&](int i) __attribute__((always_inline)) {
             i32x8 a;
+            if (i < NQK) {
+                const int sb = i / KS, ks = i % KS;
+                const u32x4 a0 = *(const u32x4*)(Kt + sb * 32 * D + koff[ks][0]);
+                const u32x4 a1 = *(const u32x4*)(Kt + sb * 32 * D + koff[ks][1]);
+                a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            } else {
+                const int db = i - NQK;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vs + u * 16 * D + voff[db]));
-                a[2 * u] = x[0];
-                a[2 * u + 1] = x[1];
+                for (int u = 0; u < 4; ++u) {
+                    const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vt + u * 16 * D + voff[db]));
+                    a[2 * u] = x[0];
+                    a[2 * u + 1] = x[1];
+                }
             }
-            oacc[db] = mfma_fp8(a, pb, oacc[db]);
+            return a;
+        };
+        __builtin_amdgcn_s_setprio(1);
+        sacc[0] = f32x16{};  // the V phase has consumed S(n)
+        sacc[1] = f32x16{};
+        i32x8 buf[AHEAD];
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) buf[i] = rd(i);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const i32x8 a = buf[i % AHEAD];
+            if (i + AHEAD < NP) buf[i % AHEAD] = rd(i + AHEAD);
+            if (i < NQK) {
+                sacc[i / KS] = mfma_fp8(a, qreg[i % KS], sacc[i / KS]);
+            } else {
+                oacc[i - NQK] = mfma_fp8(a, pb, oacc[i - NQK]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        lacc = mfma_fp8(ones, pb, lacc);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    auto vphase = [&](int n) __attribute__((always_inline)) {
+        if (active(n)) softmax(n * BN);
+    };
+    auto dma_step = [&](int k) __attribute__((always_inline)) {
+        if (k + 1 < nend) dma.issue(kb, (k + 1) * BN, S, Kbuf(k + 1), wave);
+        if (k < nend) dma.issue(vb, k * BN, S, Vbuf(k), wave);
+    };
+
+    // phase schedule of the bf16 kernel: group 0 one phase ahead of group 1
+    if (grp == 0) {
+        qk(Kbuf(0));
+        phase_barrier(false);
+        for (int n = 0; n < nend; ++n) {
+            vphase(n);
+            phase_barrier(true);
+            dma_step(n + 1);
+            mphase(n);
+            phase_barrier(false);
+        }
+        phase_barrier(true);
+    } else {
+        phase_barrier(false);
+        qk(Kbuf(0));
+        phase_barrier(true);
+        for (int n = 0; n < nend; ++n) {
+            dma_step(n + 1);
+            vphase(n);
+            phase_barrier(false);
+            mphase(n);
+            phase_barrier(true);
         }
     }
 
-    const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
-    const float ltot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
     if (qi < S) {
-        const float inv = p.vs / ltot;
+        const float l = lacc[0];
+        const float inv = p.vs / l;
         uint16_t* orow = p.out + (row0 + qi) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -238,7 +382,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(Fp8Params p) {
                                              pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv)};
             }
         }
-        if (p.lse && g == 0) p.lse[row0 + qi] = (m + __log2f(ltot) - 8.0f) * kLn2;
+        if (p.lse && g == 0) p.lse[row0 + qi] = (mc + __log2f(l) - 8.0f) * kLn2;
     }
 }
 
@@ -266,6 +410,15 @@ hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
     prm.total = (uint32_t)((int64_t)a.B * a.Hq * prm.nq);
     prm.c = a.scale * a.q_scale * a.k_scale * kLog2e;
     prm.vs = a.v_scale;
+    prm.hgrp = 0;
+    const uint32_t per = prm.total / 8u;
+    if (a.causal && per > 0 && per % (uint32_t)prm.nq == 0) {
+        const uint32_t heads_here = per / (uint32_t)prm.nq;
+        uint32_t g = (uint32_t)(kSlotsPerXcd / prm.nq > 1 ? kSlotsPerXcd / prm.nq : 1);
+        if (g > heads_here) g = heads_here;
+        while (heads_here % g) --g;
+        prm.hgrp = g;
+    }
     if (a.D == 128) return a.causal ? launch<128, true>(prm, stream) : launch<128, false>(prm, stream);
     return a.causal ? launch<64, true>(prm, stream) : launch<64, false>(prm, stream);
 }
