@@ -108,6 +108,7 @@ attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* 
  * for the product with v, and out normalised by the sum of the rounded
  * probabilities.  The ai-manual.ru tutorial (section 6) names FP8 as the next
  * factor of two after bf16.  scale, q_scale, k_scale, v_scale: finite, > 0.
+ * The codes must be finite values (not 0x7f / 0xff, e4m3fn's NaN).
  * One kernel launch, no workspace.
  * ------------------------------------------------------------------------- */
 attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse,
