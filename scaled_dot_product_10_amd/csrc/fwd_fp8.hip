@@ -28,6 +28,7 @@
 // accumulator rows (8(r/4) + 4g + r%4 of each 32-key block) in that order.
 #include "common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace attn {
 namespace {
@@ -75,19 +76,6 @@ struct Tile8 {
     __device__ static int at(int r, int chunk) { return r * D + ((chunk ^ swz(r)) << 4); }
 };
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// One global_load_lds_dwordx4: 64 lanes x 16 bytes into 1 KB of LDS at lds
-// (wave-uniform), lane L filling bytes [16L, 16L+16) from base + off.  Inline
-// assembly so later LDS reads are not ordered after it; completion is awaited
-// with s_waitcnt vmcnt(0) before the barrier that publishes the tile.  M0 is
-// reserved and reloaded by the compiler before each of its own uses.
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory");
-}
-
 // DMA of one K or V tile: wave w (< CHUNKS) fills LDS positions
 // p = 64 w + lane, i.e. row p / CPR at chunk position p % CPR, which holds
 // chunk (p % CPR) ^ swz(row); rows past the sequence repeat row S-1 (their
@@ -114,17 +102,6 @@ struct DmaPlan8 {
         }
     }
 };
-
-// Workgroup barrier between phases (see fwd_bf16.hip): LDS reads drained
-// first, with wait_dma this wave's tile DMA as well; no compiler fence.
-__device__ __forceinline__ void phase_barrier(bool wait_dma) {
-    __builtin_amdgcn_sched_barrier(0);
-    if (wait_dma)
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Params p) {
