@@ -122,9 +122,10 @@ struct DmaPlan {
 };
 
 // LOCAL (with CAUSAL): sliding window, query i sees keys i - window + 1 .. i.
-// The workgroup starts at the first key tile its first query sees; tiles
-// before a wave's own window are multiplied and fully masked, which keeps the
-// phase schedule identical to the causal one.
+// The workgroup starts at the first key tile its first query sees; a wave
+// skips the tiles before its own window (the phases still run, so the
+// schedule is the causal one), and tiles that straddle a window's left edge
+// are masked like the diagonal.
 template <int D, bool CAUSAL, bool LOCAL>
 __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     static_assert(!LOCAL || CAUSAL, "a sliding window is a causal mask");
@@ -347,6 +348,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     auto softmax = [&](int n0) __attribute__((always_inline)) { softmax_impl(n0, std::true_type{}); };
 
     auto active = [&](int n) __attribute__((always_inline)) { return !CAUSAL || n * BN <= qwmax; };
+    // LOCAL: tile n holds a key this wave's first query sees (tiles before
+    // every query's window are skipped, like tiles past the diagonal)
+    auto in_window = [&](int n) __attribute__((always_inline)) { return !LOCAL || n * BN + BN - 1 > qwmin - p.window; };
 
     phase_barrier(true);
 
@@ -358,6 +362,10 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     // other K buffer and its result is never used.
     auto mphase = [&](int n) __attribute__((always_inline)) {
         if (!active(n)) return;
+        if (LOCAL && !in_window(n)) {  // P(n) is all zero here: only S(n+1), if it counts
+            if (in_window(n + 1)) qk(Kbuf(n + 1));
+            return;
+        }
         constexpr int NQK = 2 * KS, NPV = 4 * DB, NP = NQK + NPV, AHEAD = 4;
         const char* Kt = Kbuf(n + 1);
         const char* Vt = Vbuf(n);
@@ -389,7 +397,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     };
     // V(n): softmax of tile n (from S(n) of the previous M phase)
     auto vphase = [&](int n) __attribute__((always_inline)) {
-        if (active(n)) softmax(n * BN);
+        if (active(n) && in_window(n)) softmax(n * BN);
     };
     // DMA of K(k+1) and V(k) at the start of phase 2k (k >= 1)
     auto dma_step = [&](int k) __attribute__((always_inline)) {
