@@ -64,15 +64,24 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
 }
 
 // LDS tile: BN rows x D bytes, 16-byte chunks; chunk c of row r at c ^ swz(r).
-// Row reads (16 lanes on 16 rows) and the transposed byte reads (16 lanes on
-// 8 rows, 16 bytes each) both hit distinct banks.
+// 64 banks of 4 bytes span 256 bytes: two 128-byte rows (D = 128) or four
+// 64-byte rows (D = 64).  Row reads (16 lanes on 16 rows, one chunk) need the
+// rows that share a bank span to take distinct chunks.  A transposed byte read
+// serves 32 lanes at once: 8 rows {0..3, 8..11} (or {4..7, 12..15}) x the two
+// chunks 2j, 2j+1, so those rows that share a bank span must also take
+// distinct chunk pairs, i.e. distinct swz >> 1.  At D = 128 with
+// h = (r >> 1) & 7, swz = (h2, h0, h1) (a bit permutation of h) meets both.
 template <int D>
 struct Tile8 {
     static constexpr int CPR = D / 16;
     static constexpr int BYTES = BN * D;           // 8 KB (D=128) / 4 KB (D=64)
     static constexpr int CHUNKS = BYTES / 1024;    // DMA instructions per tile
     static_assert(CHUNKS >= 1 && CHUNKS <= NW, "one DMA instruction per wave at most");
-    __device__ static int swz(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+    __device__ static int swz(int r) {
+        if (D == 64) return (r >> 2) & 3;
+        const int h = (r >> 1) & 7;
+        return (h & 4) | ((h & 1) << 1) | ((h >> 1) & 1);
+    }
     __device__ static int at(int r, int chunk) { return r * D + ((chunk ^ swz(r)) << 4); }
 };
 
