@@ -18,11 +18,16 @@
 //             one more product of an all-ones A with P(n)^T whose every row is
 //             the tile's sum of the rounded weights (the row sum l, without a
 //             vector-ALU decode of the e4m3 bytes).
-//   V phase:  mask, then p * 2^8 = 2^(s c - m + 8) rounded to e4m3.  The
-//             reference m is only raised when some score of the tile exceeds
-//             it by more than 2^0.75, which keeps every stored value below
-//             2^8.75 < 448 (the largest e4m3 value) and makes the rescaling
-//             of O and l rare.  The first tile always sets it.
+//   V phase:  mask, then 2^(s c - mc + 7) rounded to e4m3, against a storage
+//             reference mc (an integer, in scaled log2 units) that is only
+//             raised, to floor(tile max), when some score exceeds it by more
+//             than 1.75: every stored value stays below 2^8.75 < 448 (the
+//             largest e4m3 value).  O and l accumulate against a second
+//             integer reference ma <= mc; the P.V and l products take P with
+//             the E8M0 block scale 2^(mc - ma) of the MFMA (one per lane, i.e.
+//             per query and 32-key block), so raising mc costs no rescaling.
+//             Only when mc - ma would pass 64 are O and l multiplied by
+//             2^(ma - mc) and ma moved up (the first tile always does this).
 // The k order of an fp8 product only has to agree between A and B within each
 // half-wave; the transposed V reads give each lane the keys of the S^T
 // accumulator rows (8(r/4) + 4g + r%4 of each 32-key block) in that order.
@@ -37,7 +42,9 @@ constexpr int BM = 256;  // queries per workgroup
 constexpr int BN = 64;   // keys per tile
 constexpr int NW = 8;    // waves (two per SIMD)
 constexpr int NT = NW * 64;
-constexpr float kSlack = 0.75f;  // stored p * 2^8 <= 2^(8 + kSlack) < 448
+constexpr float kBias = 7.0f;    // stored weight 2^(s c - mc + kBias)
+constexpr float kRaise = 1.75f;  // s c - mc <= kRaise, so stored <= 2^8.75 < 448
+constexpr int kMaxShift = 64;    // mc - ma <= 64 keeps O and l far inside float range
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
@@ -61,6 +68,12 @@ constexpr int kSlotsPerXcd = 32;  // 32 CUs per XCD, one workgroup per CU
 // 32x32x64 e4m3 x e4m3 -> f32 (block scales 2^0)
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// the same with B scaled by the E8M0 exponent in byte 0 of sb (2^(sb - 127)):
+// lane l's scale applies to column l % 32, k block l / 32 of B (checked on
+// the hardware)
+__device__ __forceinline__ f32x16 mfma_fp8_sb(const i32x8& a, const i32x8& b, const f32x16& c, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
 // LDS tile: BN rows x D bytes, 16-byte chunks; chunk c of row r at c ^ swz(r).
@@ -196,19 +209,23 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) voff[db] = T::at(r, 2 * db + (G & 1)) + 8 * par;
     }
-    const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                        0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+    i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                  0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+    // opaque from here on: kept in registers, not rebuilt before every l product
+    asm volatile("" : "+v"(ones));
 
     const float c = p.c;
     f32x16 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-    f32x16 lacc = f32x16{};  // every row: running sum of the stored p * 2^8
-    // reference max of query qi in scaled log2 units; a finite start so that
-    // no exponent argument is inf - inf; the first tile always moves it
-    float mc = -1e30f;
+    f32x16 lacc = f32x16{};  // every row: running sum of the weights (against ma)
+    // references of query qi in scaled log2 units (integers once the first
+    // tile has set them; a finite start so that no exponent argument is
+    // inf - inf): ma for O and l, mc = ma + kx for the stored weights
+    float ma = -1e30f, mc = -1e30f;
+    int sbv = 127;  // E8M0 scale 2^kx of the stored weights in the P products
     f32x16 sacc[2];
-    i32x8 pb;
+    i32x8 pb = {};  // each V phase overwrites every byte
 
     // S^T = K.Q^T for the tile in Kt
     auto qk = [&](const uint8_t* Kt) __attribute__((always_inline)) {
@@ -225,13 +242,13 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Params p) {
         }
     };
 
-    // p * 2^8 = 2^(s c - mc + 8) -> e4m3, byte 16 sb + r of the B operand
+    // 2^(s c - mc + kBias) -> e4m3, byte 16 sb + r of the B operand
     auto exp_pack = [&](float mref) __attribute__((always_inline)) {
-        const float moff = mref - 8.0f;
+        const float moff = mref - kBias;
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
             const int sb = w >> 2, r = (w & 3) * 4;
-            int x = 0;
+            int x = pb[w];  // both halves are overwritten; no zeroing
             x = __builtin_amdgcn_cvt_pk_fp8_f32(fast_exp2(fmaf(sacc[sb][r], c, -moff)),
                                                 fast_exp2(fmaf(sacc[sb][r + 1], c, -moff)), x, false);
             x = __builtin_amdgcn_cvt_pk_fp8_f32(fast_exp2(fmaf(sacc[sb][r + 2], c, -moff)),
@@ -251,23 +268,39 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Params p) {
                     if ((CAUSAL && key > qi) || key >= S) sacc[sb][r] = -INFINITY;
                 }
         }
-        float t[16];
+        // lane max of the 32 scores: a chain of three-way maxima
+        float tmax;
+        {
+            float u[11];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) t[i] = fmaxf(sacc[0][i], sacc[1][i]);
-#pragma unroll
-        for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-            for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
-        if (__builtin_amdgcn_ballot_w64(t[0] * c > mc + kSlack)) {
-            // raise the reference to the row's tile max (both half-waves of a
-            // query agree) and rescale what was accumulated against the old one
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[0]), __float_as_uint(t[0]), false, false);
-            const float mnew = fmaxf(mc, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c);
-            const float alpha = fast_exp2(mc - mnew);  // 0 on the first tile
+            for (int i = 0; i < 10; ++i) {
+                const float a0 = i < 5 ? sacc[0][3 * i] : sacc[1][3 * (i - 5)];
+                const float a1 = i < 5 ? sacc[0][3 * i + 1] : sacc[1][3 * (i - 5) + 1];
+                const float a2 = i < 5 ? sacc[0][3 * i + 2] : sacc[1][3 * (i - 5) + 2];
+                u[i] = fmaxf(fmaxf(a0, a1), a2);
+            }
+            u[10] = fmaxf(sacc[0][15], sacc[1][15]);
+            const float v0 = fmaxf(fmaxf(u[0], u[1]), u[2]), v1 = fmaxf(fmaxf(u[3], u[4]), u[5]);
+            const float v2 = fmaxf(fmaxf(u[6], u[7]), u[8]), v3 = fmaxf(u[9], u[10]);
+            tmax = fmaxf(fmaxf(v0, v1), fmaxf(v2, v3));
+        }
+        if (__builtin_amdgcn_ballot_w64(tmax * c > mc + kRaise)) {
+            // raise mc to floor of the row's tile max (both half-waves of a
+            // query take the same value, so they keep one reference)
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+            const float mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+            mc = mt > mc + kRaise ? floorf(mt) : mc;
+            sbv = 127 + (int)fminf(mc - ma, (float)(kMaxShift + 1));
+        }
+        if (__builtin_amdgcn_ballot_w64(mc - ma > (float)kMaxShift)) {
+            // move ma up to mc: O and l by an exact power of two (0 on the
+            // first tile)
+            const float alpha = ldexpf(1.0f, (int)fmaxf(ma - mc, -256.0f));
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
             lacc *= alpha;
-            mc = mnew;
+            ma = mc;
+            sbv = 127;
         }
         exp_pack(mc);
     };
@@ -315,11 +348,11 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Params p) {
             if (i < NQK) {
                 sacc[i / KS] = mfma_fp8(a, qreg[i % KS], sacc[i / KS]);
             } else {
-                oacc[i - NQK] = mfma_fp8(a, pb, oacc[i - NQK]);
+                oacc[i - NQK] = mfma_fp8_sb(a, pb, oacc[i - NQK], sbv);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        lacc = mfma_fp8(ones, pb, lacc);
+        lacc = mfma_fp8_sb(ones, pb, lacc, sbv);
         __builtin_amdgcn_s_setprio(0);
     };
     auto vphase = [&](int n) __attribute__((always_inline)) {
@@ -368,7 +401,7 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Params p) {
                                              pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv)};
             }
         }
-        if (p.lse && g == 0) p.lse[row0 + qi] = (mc + __log2f(l) - 8.0f) * kLn2;
+        if (p.lse && g == 0) p.lse[row0 + qi] = (ma + __log2f(l) - kBias) * kLn2;
     }
 }
 

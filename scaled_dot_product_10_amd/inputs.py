@@ -151,6 +151,20 @@ def make_qkv_fp8(B: int, Hq: int, Hkv: int, S: int, D: int, seed: int):
     return to_fp8(q), to_fp8(k), to_fp8(v)
 
 
+def make_qkv_fp8_ramp(B: int, Hq: int, Hkv: int, S: int, D: int, step: float, seed: int):
+    """fp8 inputs whose scores move by about ``step`` (log2 units, after the
+    1/sqrt(D) scale) from one block of 64 keys to the next: q near the
+    all-ones vector, key j near the all-a_j vector with
+    a_j = step * (j // 64) / (sqrt(D) log2(e)), both with N(0, 0.3^2) noise,
+    v N(0,1); each quantised to e4m3fn with a power-of-two scale."""
+    rng = np.random.default_rng(seed)
+    a = step * (np.arange(S) // 64) / (np.sqrt(D) * np.log2(np.e))
+    q = 1.0 + 0.3 * rng.standard_normal((B, Hq, S, D))
+    k = a[None, None, :, None] + 0.3 * rng.standard_normal((B, Hkv, S, D))
+    v = rng.standard_normal((B, Hkv, S, D))
+    return to_fp8(q.astype(np.float32)), to_fp8(k.astype(np.float32)), to_fp8(v.astype(np.float32))
+
+
 def make_scores(B: int, H: int, S: int, D: int, seed: int) -> np.ndarray:
     """Raw (unscaled) score-like matrix ``[B,H,S,S]`` fp32 for the masked softmax alone.
 

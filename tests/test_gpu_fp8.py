@@ -2,16 +2,19 @@
 
 The inputs are the generator's N(0,1) draws rounded to e4m3fn with one
 power-of-two scale per tensor; the oracle computes exact attention on those
-values.  The kernel rounds each probability (times 2^8) to e4m3 before the
-product with v and normalises by the sum of the rounded values, so out is the
-convex combination of v rows under weights p_j (1 + e_j) + a_j with
-|e_j| <= 2^-4 (half a unit in e4m3's last place) and |a_j| <= 2^-18 (half the
-smallest subnormal step, 2^-9 / 2 / 2^8).  Hence, per element,
-    |out - ref| <= (2^-4 sw + 2^-18 su) / (1 - 2^-4 - S 2^-18 / l) + 2^-8 |ref| + 1e-5
-with sw, su the oracle's weighted and unweighted spread of v around out and
-l >= 1 the oracle's sum of p_j (max p = 1), 2^-8 |ref| covering the bf16
-store and 1e-5 the float32 sums.  lse moves by at most
--ln(1 - 2^-4 - S 2^-18) plus float32 rounding.
+values.  The kernel stores each weight as 2^(s c - mc + 7) rounded to e4m3,
+with mc an integer reference at or below the row's running max, multiplies it
+back by an exact power of two inside the P.V product, and normalises by the
+sum of the rounded values.  So out is the convex combination of v rows under
+weights p_j (1 + e_j) + a_j (max p = 1) with |e_j| <= 2^-4 (half a unit in
+e4m3's last place) and |a_j| <= 2^-17 (half the smallest subnormal step,
+2^-9 / 2, over the stored value 2^7 of a weight equal to the max).  Hence, per
+element,
+    |out - ref| <= (2^-4 sw + 2^-17 su) / (1 - 2^-4 - S 2^-17) + 2^-8 |ref| + 1e-5
+with sw, su the oracle's weighted and unweighted spread of v around out
+(l >= 1 is the oracle's sum of p_j), 2^-8 |ref| covering the bf16 store and
+1e-5 the float32 sums.  lse moves by at most -ln(1 - 2^-4 - S 2^-17) plus
+float32 rounding.
 """
 from __future__ import annotations
 
@@ -27,7 +30,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 DELTA = 2.0 ** -4
-ABS_P = 2.0 ** -18
+ABS_P = 2.0 ** -17
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -86,9 +89,24 @@ def test_c3_sampled(orc, causal):
               lse.view(-1)[idx], rows=rows)
 
 
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("step", [3.0, 20.0, 70.0, -20.0], ids=lambda s: f"step{s:+g}")
+@pytest.mark.parametrize("shape", [(1, 2, 1, 520, 64), (1, 2, 2, 300, 128)], ids=lambda s: "H{1}kv{2}S{3}D{4}".format(*s))
+def test_moving_reference(orc, shape, step, causal):
+    """Scores that rise (or fall) by `step` log2 units per 64 keys: the stored
+    weights' reference moves every block (+3), moves past 64 above the
+    accumulators' and forces their rescaling (+20 after four blocks, +70 at
+    once), or never moves and the early weights dominate (-20)."""
+    B, Hq, Hkv, S, D = shape
+    q, k, v = inputs.make_qkv_fp8_ramp(B, Hq, Hkv, S, D, step, seed=6200 + S)
+    out, lse = api.fwd_fp8(codes(q), codes(k), codes(v), q.scale, k.scale, v.scale, causal=causal)
+    torch.cuda.synchronize()
+    check_fp8(orc, f"fp8 ramp {step:+g} {shape} causal={causal}", q, k, v, causal, out, lse)
+
+
 def test_gqa_and_row0():
-    """Causal row 0 sees key 0 only: p = 2^8 exactly, so out = v_0 * v_scale
-    rounded to bf16, for every head of a GQA group."""
+    """Causal row 0 sees key 0 only: its one weight w cancels in w v / w, so
+    out = v_0 * v_scale rounded to bf16, for every head of a GQA group."""
     q, k, v = inputs.make_qkv_fp8(2, 4, 2, 300, 128, seed=6100)
     out, _ = api.fwd_fp8(codes(q), codes(k), codes(v), q.scale, k.scale, v.scale, causal=True)
     torch.cuda.synchronize()
