@@ -95,6 +95,18 @@ def time_launches(fn, iters, stream):
     return [s.elapsed_time(e) for s, e in ev]
 
 
+def settle_clock(fn, seconds):
+    """Untimed launches of fn for about ``seconds``: the clock adapts to each
+    kernel's own load within a few hundred ms."""
+    import torch
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+
+
 def cpu_baseline(q, k, v, B, Hq, S, D, sc, seconds=12.0, seed=123):
     """The fp64 CPU oracle on random rows of the same workload until ~seconds
     of wall time; rate in TFLOP/s with the same causal FLOP convention."""
@@ -137,6 +149,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--section-settle-s", type=float, default=0.3,
+                    help="untimed launches before each extra section (backward, window, fp8, decode, unfused)")
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="seconds of untimed steps before the warmup steps (clock ramp-up)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -254,6 +268,7 @@ def main():
         torch.cuda.synchronize()
         t_u = {}
         for name, f in (("qk_gemm", u1), ("masked_softmax", u2), ("pv_gemm", u3)):
+            settle_clock(f, args.section_settle_s / 3)
             t_u[name] = float(np.median(time_launches(f, 5, stream)))
         n_el = B * Hq * S * S
         # algorithmic bytes: u1 writes fp32 scores; u2 reads the unmasked (causal) part, writes bf16 p;
@@ -298,6 +313,7 @@ def main():
 
         backward()
         torch.cuda.synchronize()
+        settle_clock(backward, args.section_settle_s)
         bms = float(np.median(time_launches(backward, 10, stream)))
         bfl = 2.5 * attn_flops(B, Hq, S, D, True)
         bwd = {"workload": "causal attention backward B4 H16 S4096 D128 bf16 (dq, dk, dv)",
@@ -319,6 +335,7 @@ def main():
 
         fused_local()
         torch.cuda.synchronize()
+        settle_clock(fused_local, args.section_settle_s)
         lms = float(np.median(time_launches(fused_local, 10, stream)))
         visible = sum(min(i + 1, window) for i in range(S))
         lfl = 4.0 * B * Hq * D * visible
@@ -344,6 +361,7 @@ def main():
 
         fwd8()
         torch.cuda.synchronize()
+        settle_clock(fwd8, args.section_settle_s)
         f8ms = float(np.median(time_launches(fwd8, 20, stream)))
         f8tf = attn_flops(B, Hq, S, D, True) / (f8ms * 1e-3) / 1e12
         fp8 = {"workload": "causal attention forward B4 H16 S4096 D128, e4m3fn q/k/v, bf16 out",
@@ -376,6 +394,7 @@ def main():
 
         dec()
         torch.cuda.synchronize()
+        settle_clock(dec, args.section_settle_s)
         dms = float(np.median(time_launches(dec, 20, stream)))
         dbytes = 2 * dB * dHkv * dSkv * D * 2 + 2 * dB * dHq * D * 2 + dB * dHq * 4
         gbs_d = dbytes / (dms * 1e-3) / 1e9
