@@ -16,6 +16,9 @@ profiling; each function's C counterpart states the definition it writes out):
 * ``attn_fwd_local`` -- the same with a causal sliding window (query i sees
   its own key and the window - 1 before it): one of the special masks that
   the ai-manual.ru tutorial names as the reason for custom kernels.
+* ``attn_fwd_blockmask`` -- the same with a block mask (one flag per block
+  of 64 queries x 64 keys, combined with the causal mask): the block-sparse
+  masks of the same passages.  Rows with no visible key: out 0, lse -inf.
 * ``attn_fwd_kv`` -- Sq queries against Skv >= Sq keys and values, the
   queries being the last Sq positions (a decode step; the split-KV path).
 * ``attn_spread`` -- the spread of v around out under the attention weights
@@ -81,6 +84,10 @@ class Oracle:
         L.oracle_attn_fwd_local_rows.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64,
                                                  ctypes.c_double, ctypes.c_int, _i64, _ptr, _i64, _ptr,
                                                  _ptr, ctypes.c_int]
+        L.oracle_attn_fwd_blockmask_rows.restype = ctypes.c_int
+        L.oracle_attn_fwd_blockmask_rows.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64,
+                                                     ctypes.c_double, ctypes.c_int, _ptr, _i64, _i64, _ptr,
+                                                     _i64, _ptr, _ptr, ctypes.c_int]
         L.oracle_attn_fwd_kv_rows.restype = ctypes.c_int
         L.oracle_attn_fwd_kv_rows.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64,
                                               ctypes.c_double, ctypes.c_int, _ptr, _i64, _ptr, _ptr,
@@ -154,6 +161,32 @@ class Oracle:
                                            r.ctypes.data, r.size, out.ctypes.data,
                                            lse.ctypes.data, self._threads(nthreads))
         self._check(rc, "oracle_attn_fwd_rows")
+        if rows is None:
+            return out.reshape(B, Hq, S, D), lse.reshape(B, Hq, S)
+        return out, lse
+
+    def attn_fwd_blockmask(self, q, k, v, scale: float, causal: bool, mask, rows=None, nthreads=None):
+        """Attention with a block mask: ``mask`` is ``[Bm, Hm, nqb, nkb]``
+        (any dtype; nonzero = visible) with Bm in (1, B), Hm in (1, Hq) and
+        nqb = nkb = ceil(S / 64); a size-1 batch or head axis broadcasts.
+        Same shapes and ``rows`` as ``attn_fwd``."""
+        q, k, v = self._f32(q), self._f32(k), self._f32(v)
+        B, Hq, S, D = q.shape
+        Hkv = k.shape[1]
+        assert k.shape == (B, Hkv, S, D) and v.shape == k.shape
+        nb = (S + 63) // 64
+        m = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+        assert m.ndim == 4 and m.shape[2:] == (nb, nb) and m.shape[0] in (1, B) and m.shape[1] in (1, Hq)
+        msh = nb * nb if m.shape[1] > 1 else 0
+        msb = m.shape[1] * nb * nb if m.shape[0] > 1 else 0
+        r = self._rows(rows, B * Hq * S)
+        out = np.empty((r.size, D), dtype=np.float64)
+        lse = np.empty((r.size,), dtype=np.float64)
+        rc = self.lib.oracle_attn_fwd_blockmask_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                                     B, Hq, Hkv, S, D, float(scale), int(bool(causal)),
+                                                     m.ctypes.data, msb, msh, r.ctypes.data, r.size,
+                                                     out.ctypes.data, lse.ctypes.data, self._threads(nthreads))
+        self._check(rc, "oracle_attn_fwd_blockmask_rows")
         if rows is None:
             return out.reshape(B, Hq, S, D), lse.reshape(B, Hq, S)
         return out, lse

@@ -16,6 +16,10 @@
  *     window - 1 keys before it), one of the special masks the ai-manual.ru
  *     tutorial names (section 5's conclusions, section 7) as the reason to
  *     write custom attention kernels.
+ *   - A block mask: one flag per block of 64 queries x 64 keys says whether
+ *     the pairs in that block may attend (combined with the causal mask when
+ *     causal is set) -- the block-sparse masks of the same passages.  Rows
+ *     left with no visible key give out = 0 and lse = -inf.
  *   - The attention formula softmax(Q K^T / sqrt(d_k)) V, as stated in the
  *     "technical deep-dive" of the ainews.cool AttentionProfiler article.
  *   - The five-step causal pipeline of the Hugging Face "Profiling in PyTorch
@@ -36,10 +40,10 @@
  *     h / (Hq / Hkv) (contiguous groups); Hq must be a multiple of Hkv.
  *   - lse (log-sum-exp of a row, not on the pages): ln(sum_j exp(s_ij)) over
  *     the unmasked keys, with s already scaled.
- *   - a row with no unmasked key cannot occur (key i is always visible to
- *     query i); if it ever did, out = 0 and lse = -inf, like the "safe
- *     softmax" of the math backend described in the SDPA section of the
- *     Hugging Face article.
+ *   - a row with no unmasked key cannot occur under the causal or window
+ *     masks (key i is always visible to query i) but can under a block mask;
+ *     it gets out = 0 and lse = -inf, like the "safe softmax" of the math
+ *     backend described in the SDPA section of the Hugging Face article.
  *
  * Arithmetic: every product and sum is in double; inputs are float32 arrays
  * holding the exact values the GPU sees (bf16 values are exact in float32).
@@ -186,9 +190,32 @@ typedef struct {
     double scale;
     int causal;
     int64_t window; /* > 0: causal sliding window of this many keys */
+    /* block mask (NULL: none): flag (b, h, qb, kb) at
+     * mask[b * msb + h * msh + qb * nkb + kb], blocks of ORACLE_MASK_BLOCK */
+    const uint8_t* mask;
+    int64_t msb, msh;
     const int64_t* rows;
     double *out, *lse;
 } attn_ctx;
+
+#define ORACLE_MASK_BLOCK 64
+
+/* Whether the block mask lets query i of (b, h) see key j. */
+static int block_visible(const attn_ctx* c, int64_t b, int64_t h, int64_t i, int64_t j) {
+    if (!c->mask) return 1;
+    const int64_t nkb = (c->sh.S + ORACLE_MASK_BLOCK - 1) / ORACLE_MASK_BLOCK;
+#if ORACLE_PLANT == 15
+    const int64_t qb = j / ORACLE_MASK_BLOCK, kb = i / ORACLE_MASK_BLOCK; /* planted: blocks transposed */
+#else
+    const int64_t qb = i / ORACLE_MASK_BLOCK, kb = j / ORACLE_MASK_BLOCK;
+#endif
+#if ORACLE_PLANT == 16
+    const int64_t base = b * c->msh + h * c->msb; /* planted: batch and head strides swapped */
+#else
+    const int64_t base = b * c->msb + h * c->msh;
+#endif
+    return c->mask[base + qb * nkb + kb] != 0;
+}
 
 /*
  * For query row (b, h, i):
@@ -198,7 +225,8 @@ typedef struct {
  *   out_d = sum_j exp(s_j - m) v[b,g,j,d] / l
  *   lse   = m + ln l
  * with g the key/value head of h and J(i) = {0..i} (causal) or {0..S-1};
- * with a sliding window of W keys, J(i) = {max(0, i-W+1)..i}.
+ * with a sliding window of W keys, J(i) = {max(0, i-W+1)..i}; with a block
+ * mask, J(i) keeps only the keys whose (query block, key block) flag is set.
  * Subtracting m changes nothing mathematically; it only keeps exp finite.
  */
 static void attn_row(void* vctx, int64_t n, double* s) {
@@ -217,6 +245,10 @@ static void attn_row(void* vctx, int64_t n, double* s) {
 
     double m = -INFINITY;
     for (int64_t j = j0; j <= jl; ++j) {
+        if (!block_visible(c, b, h, i, j)) {
+            s[j] = -INFINITY; /* weight exactly 0 below */
+            continue;
+        }
         const float* kj = kb + j * D;
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d) {
@@ -234,12 +266,13 @@ static void attn_row(void* vctx, int64_t n, double* s) {
         if (s[j] > m) m = s[j];
     }
     for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
-    if (jl < 0 || m == -INFINITY) { /* no visible key: unreachable, see header */
+    if (jl < 0 || m == -INFINITY) { /* no visible key: only under a block mask */
         c->lse[n] = -INFINITY;
         return;
     }
     double l = 0.0;
     for (int64_t j = j0; j <= jl; ++j) {
+        if (s[j] == -INFINITY) continue;
 #if ORACLE_PLANT == 4
         const double w = exp(m - s[j]); /* planted: sign flipped in the exponent */
 #else
@@ -298,6 +331,41 @@ int oracle_attn_fwd_local_rows(const float* q, const float* k, const float* v,
     attn_ctx c;
     if (window > 0 && !causal) return -2;
     c.window = window;
+    c.mask = NULL;
+    c.msb = c.msh = 0;
+    c.q = q; c.k = k; c.v = v;
+    c.sh.B = B; c.sh.Hq = Hq; c.sh.Hkv = Hkv; c.sh.S = S; c.sh.D = D;
+    c.scale = scale;
+    c.causal = causal ? 1 : 0;
+    c.rows = rows;
+    c.out = out;
+    c.lse = lse;
+    int rc = check_shape(&c.sh);
+    if (rc) return rc;
+    rc = check_rows(&c.sh, rows, nrows);
+    if (rc) return rc;
+    return run_rows(attn_row, &c, nrows, S, nthreads);
+}
+
+/*
+ * As oracle_attn_fwd_rows, with a block mask: query i of (b, h) sees key j
+ * only if mask[b * msb + h * msh + (i / 64) * nkb + j / 64] != 0, with
+ * nkb = ceil(S / 64) (and j <= i when causal).  msb, msh >= 0 are element
+ * strides (0 broadcasts the mask over batches or heads).  A row with no
+ * visible key gets out = 0 and lse = -inf.
+ */
+int oracle_attn_fwd_blockmask_rows(const float* q, const float* k, const float* v,
+                                   int64_t B, int64_t Hq, int64_t Hkv, int64_t S, int64_t D,
+                                   double scale, int causal,
+                                   const uint8_t* mask, int64_t msb, int64_t msh,
+                                   const int64_t* rows, int64_t nrows,
+                                   double* out, double* lse, int nthreads) {
+    attn_ctx c;
+    if (!mask || msb < 0 || msh < 0) return -2;
+    c.window = 0;
+    c.mask = mask;
+    c.msb = msb;
+    c.msh = msh;
     c.q = q; c.k = k; c.v = v;
     c.sh.B = B; c.sh.Hq = Hq; c.sh.Hkv = Hkv; c.sh.S = S; c.sh.D = D;
     c.scale = scale;

@@ -480,6 +480,106 @@ LOCAL_PINS = [pin_local_wide_is_causal, pin_local_w1, pin_local_subproblem, pin_
 
 
 # --------------------------------------------------------------------------
+# block mask (64 x 64 blocks)
+# --------------------------------------------------------------------------
+
+def _expand_mask(mask, S):
+    """Element mask [Bm, Hm, S, S] of a block mask (each flag covers 64 x 64)."""
+    e = np.repeat(np.repeat(np.asarray(mask) != 0, 64, axis=2), 64, axis=3)
+    return e[:, :, :S, :S]
+
+
+def pin_blockmask_ones(orc):
+    """An all-ones block mask hides nothing: plain attention, bit for bit,
+    also when the mask is broadcast over batch and heads."""
+    q = _randn((2, 4, 150, 8), 130)
+    k = _randn((2, 2, 150, 8), 131)
+    v = _randn((2, 2, 150, 8), 132)
+    for causal in (True, False):
+        a, la = orc.attn_fwd(q, k, v, 0.3, causal)
+        for shape in ((1, 1, 3, 3), (2, 4, 3, 3)):
+            b, lb = orc.attn_fwd_blockmask(q, k, v, 0.3, causal, np.ones(shape, np.uint8))
+            _close(b, a, 0.0, f"ones mask {shape} causal={causal}")
+            _close(lb, la, 0.0, f"ones mask lse {shape} causal={causal}")
+
+
+def pin_blockmask_diagonal(orc):
+    """A block-diagonal mask splits the sequence into independent 64-key
+    segments: rows of segment r equal attention (causal or full) over that
+    segment alone (the pinned forward on the sliced tensors)."""
+    B, H, S, D = 1, 2, 170, 8
+    q = _randn((B, H, S, D), 133)
+    k = _randn((B, H, S, D), 134)
+    v = _randn((B, H, S, D), 135)
+    m = np.eye(3, dtype=np.uint8)[None, None]
+    for causal in (True, False):
+        out, lse = orc.attn_fwd_blockmask(q, k, v, 0.4, causal, m)
+        for r0 in (0, 64, 128):
+            r1 = min(r0 + 64, S)
+            o2, l2 = orc.attn_fwd(q[:, :, r0:r1], k[:, :, r0:r1], v[:, :, r0:r1], 0.4, causal)
+            _close(out[:, :, r0:r1], o2, 1e-14, f"segment {r0} causal={causal}")
+            _close(lse[:, :, r0:r1], l2, 1e-14, f"segment lse {r0} causal={causal}")
+
+
+def pin_blockmask_torch(orc):
+    """torch's float64 CPU scaled_dot_product_attention with the element mask
+    the block flags expand to (and j <= i when causal), on random per-(b, h)
+    masks; rows left with no visible key give out 0 and lse -inf (torch's
+    softmax would give NaN there, so those rows are checked on their own)."""
+    import torch
+
+    B, Hq, Hkv, S, D = 2, 4, 2, 150, 16
+    nb = 3
+    q = _randn((B, Hq, S, D), 136)
+    k = _randn((B, Hkv, S, D), 137)
+    v = _randn((B, Hkv, S, D), 138)
+    sc = 1 / math.sqrt(D)
+    tq = torch.from_numpy(q.astype(np.float64))
+    tk = torch.from_numpy(k.astype(np.float64)).repeat_interleave(2, dim=1)
+    tv = torch.from_numpy(v.astype(np.float64)).repeat_interleave(2, dim=1)
+    rng = _rng(139)
+    for causal in (True, False):
+        for dens in (0.3, 0.6):
+            m = (rng.random((B, Hq, nb, nb)) < dens).astype(np.uint8)
+            m[0, 1, 2, :] = 0  # one query block that sees nothing
+            em = _expand_mask(m, S)
+            if causal:
+                em = em & np.tril(np.ones((S, S), bool))[None, None]
+            out, lse = orc.attn_fwd_blockmask(q, k, v, sc, causal, m)
+            seen = em.any(axis=3)
+            ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(em),
+                                                                   scale=sc).numpy()
+            _close(out[seen], ref[seen], 1e-12, f"torch block mask causal={causal} density={dens}")
+            s = np.einsum("bhid,bhjd->bhij", q.astype(np.float64), np.repeat(k, 2, axis=1).astype(np.float64)) * sc
+            s = np.where(em, s, -np.inf)
+            mx = s.max(axis=3, keepdims=True)
+            with np.errstate(divide="ignore"):  # log 0 = -inf on the rows that see nothing
+                ref_l = (mx[..., 0] + np.log(np.exp(s - np.where(np.isfinite(mx), mx, 0)).sum(axis=3)))
+            _close(lse[seen], ref_l[seen], 1e-12, f"block mask lse causal={causal} density={dens}")
+            assert (~seen).any(), "the pin needs a row with no visible key"
+            assert np.all(out[~seen] == 0.0) and np.all(lse[~seen] == -np.inf), "empty rows: out 0, lse -inf"
+
+
+def pin_blockmask_broadcast(orc):
+    """A mask broadcast over batch (or heads) equals the same flags written
+    out for every batch (or head)."""
+    q = _randn((2, 3, 130, 8), 140)
+    k = _randn((2, 3, 130, 8), 141)
+    v = _randn((2, 3, 130, 8), 142)
+    rng = _rng(143)
+    per_head = (rng.random((1, 3, 3, 3)) < 0.5).astype(np.uint8)
+    per_batch = (rng.random((2, 1, 3, 3)) < 0.5).astype(np.uint8)
+    for m, full in ((per_head, np.repeat(per_head, 2, axis=0)), (per_batch, np.repeat(per_batch, 3, axis=1))):
+        a, la = orc.attn_fwd_blockmask(q, k, v, 0.3, False, m)
+        b, lb = orc.attn_fwd_blockmask(q, k, v, 0.3, False, full)
+        assert np.array_equal(a, b), f"broadcast {m.shape}"
+        assert np.array_equal(la, lb), f"broadcast lse {m.shape}"  # -inf rows included
+
+
+BLOCK_PINS = [pin_blockmask_ones, pin_blockmask_diagonal, pin_blockmask_torch, pin_blockmask_broadcast]
+
+
+# --------------------------------------------------------------------------
 # queries against a longer key/value sequence
 # --------------------------------------------------------------------------
 
@@ -690,4 +790,4 @@ def pin_bwd_special(orc):
 
 BWD_PINS = [pin_bwd_finite_diff, pin_bwd_torch, pin_bwd_invariants, pin_bwd_special]
 
-ALL_PINS = ATTN_PINS + STEP_PINS + LOCAL_PINS + KV_PINS + SPREAD_PINS + BWD_PINS
+ALL_PINS = ATTN_PINS + STEP_PINS + LOCAL_PINS + BLOCK_PINS + KV_PINS + SPREAD_PINS + BWD_PINS

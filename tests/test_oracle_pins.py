@@ -29,6 +29,8 @@ PLANTS = {
     12: "backward dk dv from one head of the group",
     13: "sliding window one key too wide",
     14: "decode queries aligned top-left",
+    15: "block mask transposed",
+    16: "block mask batch and head strides swapped",
 }
 
 
