@@ -61,6 +61,7 @@
 #define LIBATTN_ATTN_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -70,7 +71,8 @@ typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULL_POINTER = 1, /* a required pointer is NULL                          */
     ATTN_ERR_BAD_SHAPE = 2,    /* a size < 1, Hq % Hkv != 0, or a size overflows      */
-    ATTN_ERR_UNSUPPORTED = 3,  /* D not in {64, 128}, or causal not in {0, 1}         */
+    ATTN_ERR_UNSUPPORTED = 3,  /* D not in {64, 128}, causal not in {0, 1}, or a     */
+                               /* variant's own limit (stated with the variant)       */
     ATTN_ERR_BAD_SCALE = 4,    /* scale is not finite, or not > 0                     */
     ATTN_ERR_MISALIGNED = 5,   /* a tensor pointer breaks the alignment rule          */
     ATTN_ERR_ALIAS = 6,        /* an output overlaps an input                         */
@@ -104,8 +106,9 @@ attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* 
  * float scale per tensor.  out: bfloat16 [B,Hq,S,D]; lse: float32 [B,Hq,S] or
  * NULL.  Computes the same attention as attn_fwd_bf16 on those values, with
  * the products on the fp8 matrix cores (twice the bf16 rate): q k^T exactly
- * (fp8 products, float32 sums), the probabilities rounded to e4m3 (as p * 2^8)
- * for the product with v, and out normalised by the sum of the rounded
+ * (fp8 products, float32 sums), the probabilities rounded to e4m3 (stored
+ * against a power-of-two reference, 2^7 to 2^8.75 for the row max) for the
+ * product with v, and out normalised by the sum of the rounded
  * probabilities.  The ai-manual.ru tutorial (section 6) names FP8 as the next
  * factor of two after bf16.  scale, q_scale, k_scale, v_scale: finite, > 0.
  * The codes must be finite values (not 0x7f / 0xff, e4m3fn's NaN).
@@ -129,6 +132,32 @@ attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, void* out,
 attn_status attn_fwd_local_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
                                 int B, int Hq, int Hkv, int S, int D, float scale, int window,
                                 void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Fused forward with a block mask (bfloat16): block-sparse attention.
+ *
+ * As attn_fwd_bf16, except that query i of (b, h) sees key j only if the
+ * flag of its block pair is nonzero (and j <= i when causal = 1).  Blocks are
+ * ATTN_MASK_BLOCK queries x ATTN_MASK_BLOCK keys; with nb = ceil(S / 64), the
+ * flag of (b, h, query block qb, key block kb) is the byte
+ *     block_mask[b * mask_stride_b + h * mask_stride_h + qb * nb + kb],
+ * strides in bytes, >= 0 (0 broadcasts one mask over batches or heads).
+ * Block-sparse masks are among the special masks the ai-manual.ru tutorial
+ * gives as the reason to write custom attention kernels (section 5's
+ * conclusions, section 7).  Key tiles no query of a 256-query tile may see
+ * are neither loaded nor multiplied.  A query that sees no key gets out = 0
+ * and lse = -inf (the "safe softmax" rule of the math backend described in
+ * the SDPA section of the Hugging Face article).  block_mask is a device
+ * pointer, read only; it must not overlap out or lse (ATTN_ERR_ALIAS).
+ * S > ATTN_MASK_MAX_S returns ATTN_ERR_UNSUPPORTED.  One kernel launch, no
+ * workspace.
+ * ------------------------------------------------------------------------- */
+#define ATTN_MASK_BLOCK 64
+#define ATTN_MASK_MAX_S 131072
+attn_status attn_fwd_blockmask_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
+                                    const uint8_t* block_mask, int64_t mask_stride_b, int64_t mask_stride_h,
+                                    int B, int Hq, int Hkv, int S, int D, float scale, int causal,
+                                    void* stream);
 
 /* ---------------------------------------------------------------------------
  * Split-KV forward for short query counts (bfloat16): a decode step.

@@ -27,6 +27,7 @@ STATUS = {
 _p = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
+_i64 = ctypes.c_int64
 
 # symbol -> (restype, argtypes)
 SIGNATURES = {
@@ -34,6 +35,7 @@ SIGNATURES = {
     "attn_fwd_f32": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "attn_fwd_fp8": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _f, _f, _f, _i, _p]),
     "attn_fwd_local_bf16": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
+    "attn_fwd_blockmask_bf16": (_i, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i, _i, _i, _i, _i, _f, _i, _p]),
     "attn_qk_gemm_bf16": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "attn_qk_gemm_f32": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "attn_masked_softmax_bf16": (_i, [_p, _p, _p, _i, _i, _i, _f, _i, _p]),
@@ -99,6 +101,12 @@ def attn_fwd_fp8(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, q_scale, k_scale, v
 
 def attn_fwd_local_bf16(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, window, stream) -> int:
     return _call("attn_fwd_local_bf16", q, k, v, out, lse, B, Hq, Hkv, S, D, scale, window, stream)
+
+
+def attn_fwd_blockmask_bf16(q, k, v, out, lse, block_mask, mask_stride_b, mask_stride_h, B, Hq, Hkv, S, D, scale,
+                            causal, stream) -> int:
+    return _call("attn_fwd_blockmask_bf16", q, k, v, out, lse, block_mask, mask_stride_b, mask_stride_h, B, Hq, Hkv,
+                 S, D, scale, causal, stream)
 
 
 def attn_qk_gemm_bf16(q, k, scores, B, Hq, Hkv, S, D, stream) -> int:

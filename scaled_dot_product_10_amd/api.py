@@ -40,12 +40,18 @@ def _raise(code: int, name: str):
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = True, scale: float | None = None,
-        out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True, window: int | None = None):
+        out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True, window: int | None = None,
+        block_mask: torch.Tensor | None = None):
     """Fused attention forward.  q ``[B,Hq,S,D]``, k/v ``[B,Hkv,S,D]``, bf16 or fp32.
 
     Returns ``(out, lse)``; ``lse`` is float32 ``[B,Hq,S]`` (None if ``lse=False``).
     ``scale`` defaults to 1/sqrt(D).  ``window`` (bf16, causal only): each query
     sees its own key and the ``window - 1`` before it (``attn_fwd_local_bf16``).
+    ``block_mask`` (bf16): bool or uint8 ``[Bm, Hm, nb, nb]`` on the device,
+    nb = ceil(S / 64), Bm in (1, B), Hm in (1, Hq) (size-1 or stride-0 axes
+    broadcast), last two axes contiguous; nonzero = the 64 x 64 block of
+    (query, key) pairs is visible, combined with ``causal``
+    (``attn_fwd_blockmask_bf16``).  Queries that see no key: out 0, lse -inf.
     """
     if q.dtype not in _SUFFIX:
         raise TypeError(f"unsupported dtype {q.dtype}")
@@ -68,6 +74,26 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Tru
     elif lse is not None:
         _check(lse, "lse", torch.float32, 3)
     lp = lse.data_ptr() if lse is not None else None
+    if block_mask is not None:
+        if q.dtype != torch.bfloat16 or window is not None:
+            raise ValueError("a block mask needs bf16 tensors and no window")
+        nb = (S + 63) // 64
+        m = block_mask
+        if m.dtype == torch.bool:
+            m = m.view(torch.uint8)
+        if m.dtype != torch.uint8 or m.device != q.device or m.dim() != 4:
+            raise ValueError("block_mask must be a 4-d bool or uint8 tensor on q's device")
+        if tuple(m.shape[2:]) != (nb, nb) or m.shape[0] not in (1, B) or m.shape[1] not in (1, Hq):
+            raise ValueError(f"block_mask shape {tuple(m.shape)}: expected [1 or {B}, 1 or {Hq}, {nb}, {nb}]")
+        if m.stride(3) != 1 or m.stride(2) != nb:
+            raise ValueError("block_mask: the last two axes must be contiguous")
+        sb = m.stride(0) if m.shape[0] > 1 else 0
+        sh = m.stride(1) if m.shape[1] > 1 else 0
+        code = _lib.attn_fwd_blockmask_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lp,
+                                            m.data_ptr(), sb, sh, B, Hq, Hkv, S, D, float(scale),
+                                            int(bool(causal)), _stream(q.device))
+        _raise(code, "attn_fwd_blockmask_bf16")
+        return out, lse
     if window is not None:
         if q.dtype != torch.bfloat16 or not causal:
             raise ValueError("a sliding window needs bf16 tensors and causal=True")

@@ -188,6 +188,29 @@ attn_status attn_fwd_local_bf16(const void* q, const void* k, const void* v, voi
     return hip_status(attn::launch_fwd_bf16(a, (hipStream_t)stream));
 }
 
+attn_status attn_fwd_blockmask_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
+                                    const uint8_t* block_mask, int64_t mask_stride_b, int64_t mask_stride_h, int B,
+                                    int Hq, int Hkv, int S, int D, float scale, int causal, void* stream) {
+    const attn_status st = check_fwd(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, 2);
+    if (st != ATTN_OK) return st;
+    if (!block_mask) return ATTN_ERR_NULL_POINTER;
+    if (S > ATTN_MASK_MAX_S) return ATTN_ERR_UNSUPPORTED;
+    if (mask_stride_b < 0 || mask_stride_h < 0) return ATTN_ERR_BAD_SHAPE;
+    const int64_t nb = (S + ATTN_MASK_BLOCK - 1) / ATTN_MASK_BLOCK;
+    // bytes from block_mask to one past its last flag
+    const int64_t lim = int64_t(1) << 60;
+    if (mask_stride_b > lim / B || mask_stride_h > lim / Hq) return ATTN_ERR_BAD_SHAPE;
+    const int64_t extent = (int64_t)(B - 1) * mask_stride_b + (int64_t)(Hq - 1) * mask_stride_h + nb * nb;
+    const int64_t no = prod({B, Hq, S, D, 2});
+    const int64_t nl = prod({B, Hq, S, 4});
+    if (overlap(out, no, block_mask, extent) || overlap(lse, nl, block_mask, extent)) return ATTN_ERR_ALIAS;
+    attn::FwdArgs a = fwd_args(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal);
+    a.bmask = block_mask;
+    a.bmask_stride_b = mask_stride_b;
+    a.bmask_stride_h = mask_stride_h;
+    return hip_status(attn::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
 attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
                          int S, int D, float scale, float q_scale, float k_scale, float v_scale, int causal,
                          void* stream) {

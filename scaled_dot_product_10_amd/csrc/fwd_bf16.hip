@@ -38,6 +38,10 @@
 //   wave skips the work of tiles past its own last query, and only tiles that
 //   straddle the diagonal (or the end of the sequence) apply the mask.
 //   Causal workgroups start with the longest query tiles.
+//   Block mask (one flag per 64 queries x 64 keys): each workgroup first lists
+//   the key tiles any of its four query blocks may see and runs the same
+//   phase schedule over that list only; a wave gives P = 0 to the listed
+//   tiles its own block may not see.
 #include <type_traits>
 
 #include "common.h"
@@ -52,6 +56,9 @@ constexpr int BN = 64;    // keys per tile
 constexpr int NW = 8;     // waves per workgroup (two per SIMD)
 constexpr int NT = NW * 64;
 constexpr float kMaxTileSum = 4096.0f;  // bound on one lane tile sum of p (so p <= 2^12)
+constexpr int kMaskBlock = 64;          // block-mask granularity (queries and keys); == BN
+constexpr int kMaxMaskTiles = 2048;     // key tiles a block-masked launch may have (S <= 131072)
+static_assert(kMaskBlock == BN && BM % kMaskBlock == 0 && BM / kMaskBlock <= 8, "mask blocks vs tiles");
 
 struct Params {
     const uint16_t* q;
@@ -64,6 +71,10 @@ struct Params {
     uint32_t hgrp;  // causal: heads whose tiles one XCD runs together (0: plain order)
     float c;        // scale * log2(e), > 0
     int window;     // LOCAL: keys each query sees (its own and window - 1 before it)
+    // BLOCK: flag (b, h, qb, kb) at bmask[b * bm_sb + h * bm_sh + qb * nkb + kb]
+    const uint8_t* bmask;
+    int64_t bm_sb, bm_sh;
+    int nkb;
 };
 
 // Workgroups one XCD holds at once: 32 CUs per XCD, one 8-wave workgroup per CU.
@@ -126,14 +137,21 @@ struct DmaPlan {
 // skips the tiles before its own window (the phases still run, so the
 // schedule is the causal one), and tiles that straddle a window's left edge
 // are masked like the diagonal.
-template <int D, bool CAUSAL, bool LOCAL>
+// BLOCK: the loop runs over positions 0 .. npos-1 of the workgroup's list of
+// key tiles (tile number and one flag per query block); buffers alternate by
+// position.  Otherwise position n is tile n.
+template <int D, bool CAUSAL, bool LOCAL, bool BLOCK>
 __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     static_assert(!LOCAL || CAUSAL, "a sliding window is a causal mask");
+    static_assert(!(LOCAL && BLOCK), "one mask kind at a time");
     using T = Tile<D>;
     constexpr int KS = D / 16;  // k-steps of the Q.K^T product
     constexpr int DB = D / 32;  // 32-row blocks of O^T
     constexpr int ROWB = T::CPR * 16;  // bytes per tile row
     __shared__ __attribute__((aligned(1024))) char smem[4 * T::BYTES];
+    // BLOCK: listed key tiles (bits 0-23 tile, bit 24 + j: query block j may see it)
+    __shared__ uint32_t blist[BLOCK ? kMaxMaskTiles + 2 : 1];
+    __shared__ int bcount[BLOCK ? NW : 1];
     // K buffers at [0, 2*BYTES), V buffers at [2*BYTES, 4*BYTES)
     auto Kbuf = [&](int i) __attribute__((always_inline)) { return smem + (i & 1) * T::BYTES; };
     auto Vbuf = [&](int i) __attribute__((always_inline)) { return smem + (2 + (i & 1)) * T::BYTES; };
@@ -186,17 +204,73 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
 
     const int qlast = min(m0 + BM, S) - 1;
     const int ntiles = (S + BN - 1) / BN;
-    const int nend = CAUSAL ? min(ntiles, qlast / BN + 1) : ntiles;
+    int nend = CAUSAL ? min(ntiles, qlast / BN + 1) : ntiles;
     const int nbeg = LOCAL ? max(0, m0 - p.window + 1) / BN : 0;
+
+    if (BLOCK) {
+        // list the tiles below nend that a query block of this workgroup may
+        // see, in order: flags per thread, then a ballot/popcount compaction
+        const int qb0 = m0 / kMaskBlock;
+        const int nqb = min(BM / kMaskBlock, (S - m0 + kMaskBlock - 1) / kMaskBlock);
+        const uint8_t* mrow = p.bmask + (int64_t)b * p.bm_sb + (int64_t)h * p.bm_sh + (int64_t)qb0 * p.nkb;
+        int base = 0;
+        for (int t0 = 0; t0 < nend; t0 += NT) {
+            const int t = t0 + tid;
+            uint32_t bits = 0;
+            if (t < nend) {
+#pragma unroll
+                for (int j = 0; j < BM / kMaskBlock; ++j)
+                    if (j < nqb && mrow[(int64_t)j * p.nkb + t]) bits |= 1u << j;
+            }
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(bits != 0);
+            const int within = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (lane == 0) bcount[wave] = __builtin_popcountll(bal);
+            __syncthreads();
+            int before = 0, total = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int cw = bcount[w];
+                before += w < wave ? cw : 0;
+                total += cw;
+            }
+            if (bits) blist[base + before + within] = (uint32_t)t | (bits << 24);
+            base += total;
+            __syncthreads();
+        }
+        if (tid < 2) blist[base + tid] = 0;  // the two positions after the last: tile 0, no block
+        __syncthreads();
+        nend = base;
+        if (nend == 0) {  // no key visible to any query of this workgroup
+            if (qi < S) {
+                uint16_t* orow = p.out + (row0 + qi) * D;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) *(u32x2*)(orow + db * 32 + j * 8 + g * 4) = u32x2{0u, 0u};
+                if (p.lse && g == 0) p.lse[row0 + qi] = -INFINITY;
+            }
+            return;
+        }
+    }
+    // Entry of position n (BLOCK: the list entry; otherwise n itself), read
+    // once per loop iteration; the key tile it names, and whether this wave's
+    // query block may see that tile.
+    auto ent = [&](int n) __attribute__((always_inline)) {
+        return BLOCK ? __builtin_amdgcn_readfirstlane(blist[n]) : (uint32_t)n;
+    };
+    auto tile_of = [&](uint32_t e) __attribute__((always_inline)) { return BLOCK ? (int)(e & 0xffffffu) : (int)e; };
+    auto wave_sees = [&](uint32_t e) __attribute__((always_inline)) {
+        return !BLOCK || ((e >> (24 + wave / 2)) & 1u) != 0;
+    };
 
     // ---- prologue: K(nbeg), V(nbeg), K(nbeg+1) in flight while Q is loaded --
     DmaPlan<D, false> kdma;
     DmaPlan<D, true> vdma;
     kdma.init(wave, lane);
     vdma.init(wave, lane);
-    kdma.issue(kb, nbeg * BN, S, Kbuf(nbeg), wave);
-    vdma.issue(vb, nbeg * BN, S, Vbuf(nbeg), wave);
-    if (nbeg + 1 < nend) kdma.issue(kb, (nbeg + 1) * BN, S, Kbuf(nbeg + 1), wave);
+    kdma.issue(kb, tile_of(ent(nbeg)) * BN, S, Kbuf(nbeg), wave);
+    vdma.issue(vb, tile_of(ent(nbeg)) * BN, S, Vbuf(nbeg), wave);
+    if (nbeg + 1 < nend) kdma.issue(kb, tile_of(ent(nbeg + 1)) * BN, S, Kbuf(nbeg + 1), wave);
 
     // Q operand (B of S^T = K.Q^T): query qi, d = 16*ks + 8*g .. +7.
     bf16x8 qreg[KS];
@@ -347,10 +421,12 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     };
     auto softmax = [&](int n0) __attribute__((always_inline)) { softmax_impl(n0, std::true_type{}); };
 
-    auto active = [&](int n) __attribute__((always_inline)) { return !CAUSAL || n * BN <= qwmax; };
-    // LOCAL: tile n holds a key this wave's first query sees (tiles before
+    auto active = [&](uint32_t e) __attribute__((always_inline)) { return !CAUSAL || tile_of(e) * BN <= qwmax; };
+    // LOCAL: the tile holds a key this wave's first query sees (tiles before
     // every query's window are skipped, like tiles past the diagonal)
-    auto in_window = [&](int n) __attribute__((always_inline)) { return !LOCAL || n * BN + BN - 1 > qwmin - p.window; };
+    auto in_window = [&](uint32_t e) __attribute__((always_inline)) {
+        return !LOCAL || tile_of(e) * BN + BN - 1 > qwmin - p.window;
+    };
 
     phase_barrier(true);
 
@@ -360,10 +436,10 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     // hoisting reads further, which would only cost registers).  One code
     // path: for the last tile the S(n+1) product reads the (stale, in-bounds)
     // other K buffer and its result is never used.
-    auto mphase = [&](int n) __attribute__((always_inline)) {
-        if (!active(n)) return;
-        if (LOCAL && !in_window(n)) {  // P(n) is all zero here: only S(n+1), if it counts
-            if (in_window(n + 1)) qk(Kbuf(n + 1));
+    auto mphase = [&](int n, uint32_t e0, uint32_t e1) __attribute__((always_inline)) {
+        if (!active(e0)) return;
+        if (LOCAL && !in_window(e0)) {  // P(n) is all zero here: only S(n+1), if it counts
+            if (in_window(e1)) qk(Kbuf(n + 1));
             return;
         }
         constexpr int NQK = 2 * KS, NPV = 4 * DB, NP = NQK + NPV, AHEAD = 4;
@@ -396,13 +472,24 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
         __builtin_amdgcn_s_setprio(0);
     };
     // V(n): softmax of tile n (from S(n) of the previous M phase)
-    auto vphase = [&](int n) __attribute__((always_inline)) {
-        if (active(n) && in_window(n)) softmax(n * BN);
+    // BLOCK: a listed tile this wave's block may not see gets P = 0 (the
+    // matrix phase runs as usual: the workgroup's phases take as long as
+    // their busiest wave anyway)
+    auto vphase = [&](uint32_t e0) __attribute__((always_inline)) {
+        if (active(e0) && in_window(e0)) {
+            if (wave_sees(e0)) {
+                softmax(tile_of(e0) * BN);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pb[i] = bf16x8{};
+            }
+        }
     };
-    // DMA of K(k+1) and V(k) at the start of phase 2k (k >= 1)
-    auto dma_step = [&](int k) __attribute__((always_inline)) {
-        if (k + 1 < nend) kdma.issue(kb, (k + 1) * BN, S, Kbuf(k + 1), wave);
-        if (k < nend) vdma.issue(vb, k * BN, S, Vbuf(k), wave);
+    // DMA of K(k+1) and V(k) at the start of phase 2k (k >= 1); ek, ek1 the
+    // entries of positions k, k+1
+    auto dma_step = [&](int k, uint32_t ek, uint32_t ek1) __attribute__((always_inline)) {
+        if (k + 1 < nend) kdma.issue(kb, tile_of(ek1) * BN, S, Kbuf(k + 1), wave);
+        if (k < nend) vdma.issue(vb, tile_of(ek) * BN, S, Vbuf(k), wave);
     };
 
     // Phase schedule (barrier after every phase; odd phases also wait for the
@@ -420,10 +507,11 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
         qk(Kbuf(nbeg));
         phase_barrier(false);
         for (int n = nbeg; n < nend; ++n) {
-            vphase(n);
+            const uint32_t e0 = ent(n), e1 = ent(n + 1), e2 = ent(n + 2);
+            vphase(e0);
             phase_barrier(true);
-            dma_step(n + 1);
-            mphase(n);
+            dma_step(n + 1, e1, e2);
+            mphase(n, e0, e1);
             phase_barrier(false);
         }
         phase_barrier(true);
@@ -432,10 +520,11 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
         qk(Kbuf(nbeg));
         phase_barrier(true);
         for (int n = nbeg; n < nend; ++n) {
-            dma_step(n + 1);
-            vphase(n);
+            const uint32_t e0 = ent(n), e1 = ent(n + 1), e2 = ent(n + 2);
+            dma_step(n + 1, e1, e2);
+            vphase(e0);
             phase_barrier(false);
-            mphase(n);
+            mphase(n, e0, e1);
             phase_barrier(true);
         }
     }
@@ -444,7 +533,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
     const float ltot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
     if (qi < S) {
-        const float inv = 1.0f / ltot;
+        // BLOCK: a query block that sees no listed tile has l = 0: out 0, lse -inf
+        const bool seen = !BLOCK || ltot > 0.f;
+        const float inv = seen ? 1.0f / ltot : 0.f;
         uint16_t* orow = p.out + (row0 + qi) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -456,16 +547,16 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
                 *(u32x2*)(orow + d0) = w;
             }
         }
-        if (p.lse && g == 0) p.lse[row0 + qi] = (mc + __log2f(ltot)) * kLn2;
+        if (p.lse && g == 0) p.lse[row0 + qi] = seen ? (mc + __log2f(ltot)) * kLn2 : -INFINITY;
     }
 }
 
-template <int D, bool CAUSAL, bool LOCAL = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BLOCK = false>
 hipError_t launch(const Params& prm, hipStream_t stream) {
     Params arg = prm;
     void* args[] = {&arg};
-    return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, CAUSAL, LOCAL>, dim3(prm.total), dim3(NT), args, 0,
-                           stream);
+    return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, CAUSAL, LOCAL, BLOCK>, dim3(prm.total), dim3(NT), args,
+                           0, stream);
 }
 
 }  // namespace
@@ -485,6 +576,10 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     prm.total = (uint32_t)((int64_t)a.B * a.Hq * prm.nq);
     prm.c = a.scale * kLog2e;
     prm.window = a.window;
+    prm.bmask = a.bmask;
+    prm.bm_sb = a.bmask_stride_b;
+    prm.bm_sh = a.bmask_stride_h;
+    prm.nkb = (a.S + kMaskBlock - 1) / kMaskBlock;
     prm.hgrp = 0;
     const uint32_t per = prm.total / 8u;
     if (per > 0 && per % (uint32_t)prm.nq == 0) {
@@ -493,6 +588,10 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
         if (g > heads_here) g = heads_here;
         while (heads_here % g) --g;
         prm.hgrp = g;
+    }
+    if (a.bmask) {
+        if (a.D == 128) return a.causal ? launch<128, true, false, true>(prm, stream) : launch<128, false, false, true>(prm, stream);
+        return a.causal ? launch<64, true, false, true>(prm, stream) : launch<64, false, false, true>(prm, stream);
     }
     // a window of at least S keys hides nothing the causal mask shows
     if (a.causal && a.window > 0 && a.window < a.S)

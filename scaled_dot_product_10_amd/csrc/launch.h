@@ -17,6 +17,10 @@ struct FwdArgs {
     float scale;  // > 0, finite
     int causal;   // 0 or 1
     int window;   // 0: none; >= 1 (bf16, causal only): sliding window of this many keys
+    // bf16 only: block mask, one byte per 64 x 64 block at
+    // bmask[b * bmask_stride_b + h * bmask_stride_h + qb * ceil(S/64) + kb]; null: none
+    const uint8_t* bmask = nullptr;
+    int64_t bmask_stride_b = 0, bmask_stride_h = 0;
 };
 
 struct QkArgs {

@@ -40,7 +40,7 @@ def L():
 
 def test_header_symbols_are_exported(L):
     syms = header_symbols()
-    assert len(syms) == 19, syms
+    assert len(syms) == 20, syms
     nm = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)], capture_output=True, text=True,
                         check=True).stdout
     exported = set(re.findall(r"\bT (\w+)$", nm, flags=re.M))
@@ -133,6 +133,31 @@ def test_local_rejects():
     assert f(None, *args[1:], 4, None) == NULL
     assert f(A, Bp, C, A, E, 1, 2, 1, 16, 64, 0.125, 4, None) == ALIAS
     assert f(A, Bp, C, Dp, E, 1, 2, 1, 16, 64, float("nan"), 4, None) == SCALE
+
+
+def test_blockmask_rejects():
+    f = _lib.attn_fwd_blockmask_bf16
+    M = E + (1 << 24)  # a mask range apart from every tensor
+
+    def call(**kw):
+        a = dict(q=A, k=Bp, v=C, out=Dp, lse=E, mask=M, sb=0, sh=0, B=2, Hq=4, Hkv=2, S=300, D=64, scale=0.125,
+                 causal=1, stream=None)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(mask=None) == NULL
+    assert call(q=None) == NULL
+    assert call(S=131073) == UNSUP
+    assert call(D=96) == UNSUP
+    assert call(causal=2) == UNSUP
+    assert call(sb=-1) == SHAPE
+    assert call(sh=-5) == SHAPE
+    assert call(sb=1 << 62) == SHAPE
+    assert call(scale=float("inf")) == SCALE
+    assert call(mask=Dp + 100) == ALIAS  # inside out
+    assert call(mask=E + 8) == ALIAS     # inside lse
+    assert call(mask=Dp - 10, sb=0, sh=0) == ALIAS  # 25 flags (5 x 5 blocks) reach into out
+    assert call(out=Bp) == ALIAS
 
 
 def test_splitkv_rejects_and_sizes():
