@@ -146,6 +146,7 @@ def main():
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-local", action="store_true")
+    ap.add_argument("--no-blockmask", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -342,6 +343,46 @@ def main():
         local = {"workload": f"causal sliding window W={window}, B4 H16 S4096 D128 bf16", "window": window,
                  "ms": round(lms, 4), "tflops": round(lfl / (lms * 1e-3) / 1e12, 2), "flops": lfl}
 
+    # block-sparse causal forward on the same inputs (attn_fwd_blockmask_bf16):
+    # one 64x64 block mask for every head -- a band of 4 blocks ending at the
+    # diagonal, the first 2 key blocks, and 10% of the other blocks at random
+    # (numpy seed 11) -- combined with the causal mask; FLOPs over visible pairs
+    blockmask = None
+    if not args.no_blockmask:
+        nb = (S + 63) // 64
+        rng_b = np.random.default_rng(11)
+        mb = rng_b.random((nb, nb)) < 0.1
+        for i in range(nb):
+            mb[i, max(0, i - 3):i + 1] = True
+            mb[i, :2] = True
+        mb &= np.tril(np.ones((nb, nb), bool))
+        mask_d = torch.from_numpy(mb.astype(np.uint8)).to(dev).view(1, 1, nb, nb)
+        # visible (query, key) pairs: full blocks below the diagonal, triangles on it
+        rows_in = np.minimum(64, S - 64 * np.arange(nb))
+        pairs = sum(int(rows_in[i]) * int(rows_in[j]) if j < i else int(rows_in[i]) * (int(rows_in[i]) + 1) // 2
+                    for i, j in zip(*np.nonzero(mb)))
+        # key tiles the workgroups run: per 256-query tile, the union of its 4 block rows
+        wg_tiles = sum(int(mb[4 * t:4 * t + 4].any(axis=0).sum()) for t in range((nb + 3) // 4))
+        causal_tiles = sum(min(nb, 4 * t + 4) for t in range((nb + 3) // 4))
+
+        def fused_block():
+            rc = _lib.attn_fwd_blockmask_bf16(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(),
+                                              lse.data_ptr(), mask_d.data_ptr(), 0, 0, B, Hq, Hkv, S, D, sc, 1, sp)
+            if rc:
+                raise _lib.AttnError(rc, "attn_fwd_blockmask_bf16")
+
+        fused_block()
+        torch.cuda.synchronize()
+        settle_clock(fused_block, args.section_settle_s)
+        bms_ = float(np.median(time_launches(fused_block, 10, stream)))
+        bfl_ = 4.0 * B * Hq * D * pairs
+        blockmask = {"workload": "causal block-sparse B4 H16 S4096 D128 bf16: 64x64 blocks, band of 4 + first 2 "
+                                 "key blocks + 10% random (seed 11), same mask for every head",
+                     "visible_frac_of_causal": round(pairs / (S * (S + 1) / 2), 4),
+                     "tile_frac_of_causal": round(wg_tiles / causal_tiles, 4),
+                     "ms": round(bms_, 4), "tflops": round(bfl_ / (bms_ * 1e-3) / 1e12, 2), "flops": bfl_}
+        del mask_d
+
     # fp8 forward on the same shape: N(0,1) draws in e4m3fn with one power-of-two
     # scale per tensor (2^-6 keeps max |x| < 448 * 2^-6 = 7)
     fp8 = None
@@ -433,6 +474,7 @@ def main():
         "unfused": unfused,
         "backward": bwd,
         "local": local,
+        "blockmask": blockmask,
         "decode": decode,
         "fp8": fp8,
         "gpu": props.name,
