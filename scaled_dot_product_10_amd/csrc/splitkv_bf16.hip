@@ -16,7 +16,8 @@
 //   query rows, split).  The rows are the (query head of g's group, query)
 //   pairs, so a GQA group's heads share every K/V tile.  Q is the MFMA B
 //   operand (row r = lane % 32) for the whole split; 128-key chunks of K and V
-//   pass through LDS (whole-row loads), each wave takes 32 keys of a chunk and
+//   pass through LDS (whole-row loads, the next chunk in flight while the
+//   current one is processed), each wave takes 32 keys of a chunk and
 //   keeps its own running max, sum and O^T; the four waves merge through LDS
 //   at the end.  The kernel is bound by the K/V read: its arithmetic is a
 //   small fraction of the matrix cores' rate.
@@ -103,14 +104,21 @@ __global__ __launch_bounds__(NT, 2) void splitkv_bf16_kernel(SkvParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
 
+    // chunk k0 + CHUNK is loaded into registers while chunk k0 is processed
     TKV tk, tv;
+    if (k_lo < k_hi) {
+        tk.load(kb, k_lo, k_hi, tid);  // rows at or past k_hi are zero (and masked below)
+        tv.load(vb, k_lo, k_hi, tid);
+    }
     for (int k0 = k_lo; k0 < k_hi; k0 += CHUNK) {
-        tk.load(kb, k0, k_hi, tid);  // rows at or past k_hi are zero (and masked below)
-        tv.load(vb, k0, k_hi, tid);
         __syncthreads();  // previous chunk consumed
         tk.store(Ks, tid);
         tv.store(Vs, tid);
         __syncthreads();
+        if (k0 + CHUNK < k_hi) {
+            tk.load(kb, k0 + CHUNK, k_hi, tid);
+            tv.load(vb, k0 + CHUNK, k_hi, tid);
+        }
         const int kw = k0 + wave * 32;  // this wave's first key
         if (kw >= k_hi) continue;
         f32x16 sacc = f32x16{};
