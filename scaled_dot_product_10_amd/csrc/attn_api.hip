@@ -361,7 +361,7 @@ attn_status attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, v
     const int64_t nws = splitkv_ws_floats(B, Hq, Sq, D, nsplit);
     if (nq < 0 || nkv < 0 || nl < 0 || nws < 0 || nws > (int64_t(1) << 60) / 4) return ATTN_ERR_BAD_SHAPE;
     if (prod({B, Hkv, attn::splitkv_row_blocks(Hq, Hkv, Sq), nsplit}) > kMaxGrid ||
-        prod({B, Hq, Sq, D}) > kMaxGrid * 256LL)
+        prod({B, Hq, Sq}) > kMaxGrid)  // the merge runs one workgroup per query row
         return ATTN_ERR_BAD_SHAPE;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
         misaligned(workspace, 16) || misaligned(lse, 4))

@@ -21,7 +21,7 @@
 //   keeps its own running max, sum and O^T; the four waves merge through LDS
 //   at the end.  The kernel is bound by the K/V read: its arithmetic is a
 //   small fraction of the matrix cores' rate.
-// splitkv_merge_kernel: one thread per (row, d).
+// splitkv_merge_kernel: one workgroup per row.
 #include "common.h"
 #include "launch.h"
 #include "lds_tiles.h"
@@ -32,6 +32,7 @@ namespace {
 constexpr int NT = 256;        // 4 waves
 constexpr int ROWS = 32;       // packed query rows per workgroup (MFMA columns)
 constexpr int CHUNK = 128;     // keys per workgroup step (32 per wave)
+constexpr int kMaxMergeSplits = 4096;  // splits the merge holds in LDS (the entry point's limit)
 
 struct SkvParams {
     const uint16_t* q;
@@ -104,20 +105,30 @@ __global__ __launch_bounds__(NT, 2) void splitkv_bf16_kernel(SkvParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
 
-    // chunk k0 + CHUNK is loaded into registers while chunk k0 is processed
+    // The split's chunks are taken in a rotated order, different per
+    // workgroup, so that workgroups streaming equally aligned slices do not
+    // hit the same memory channels in step.  The next chunk is loaded into
+    // registers while the current one is processed.
+    const int nch = (k_hi - k_lo + CHUNK - 1) / CHUNK;
+    const int rot = nch > 0 ? (int)((L * 7u) % (uint32_t)nch) : 0;
+    auto chunk = [&](int i) __attribute__((always_inline)) {
+        const int j = i + rot;
+        return k_lo + (j < nch ? j : j - nch) * CHUNK;
+    };
     TKV tk, tv;
-    if (k_lo < k_hi) {
-        tk.load(kb, k_lo, k_hi, tid);  // rows at or past k_hi are zero (and masked below)
-        tv.load(vb, k_lo, k_hi, tid);
+    if (nch > 0) {
+        tk.load(kb, chunk(0), k_hi, tid);  // rows at or past k_hi are zero (and masked below)
+        tv.load(vb, chunk(0), k_hi, tid);
     }
-    for (int k0 = k_lo; k0 < k_hi; k0 += CHUNK) {
+    for (int i = 0; i < nch; ++i) {
+        const int k0 = chunk(i);
         __syncthreads();  // previous chunk consumed
         tk.store(Ks, tid);
         tv.store(Vs, tid);
         __syncthreads();
-        if (k0 + CHUNK < k_hi) {
-            tk.load(kb, k0 + CHUNK, k_hi, tid);
-            tv.load(vb, k0 + CHUNK, k_hi, tid);
+        if (i + 1 < nch) {
+            tk.load(kb, chunk(i + 1), k_hi, tid);
+            tv.load(vb, chunk(i + 1), k_hi, tid);
         }
         const int kw = k0 + wave * 32;  // this wave's first key
         if (kw >= k_hi) continue;
@@ -206,24 +217,70 @@ __global__ __launch_bounds__(NT, 2) void splitkv_bf16_kernel(SkvParams p) {
 }
 
 // out = sum_s e^{lse_s - lse} out_s, lse = ln sum_s e^{lse_s}; one thread per (row, d)
+// Workgroup-wide max / sum of one value per thread (all NT threads call it).
+__device__ __forceinline__ float block_reduce(float x, bool is_max, float* scratch) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float y = __shfl_xor(x, o, 64);
+        x = is_max ? fmaxf(x, y) : x + y;
+    }
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) scratch[wave] = x;
+    __syncthreads();
+    float r = scratch[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) r = is_max ? fmaxf(r, scratch[w]) : r + scratch[w];
+    __syncthreads();  // scratch reusable
+    return r;
+}
+
+// One workgroup per row: the split weights w_s = e^{lse_s - M} are computed
+// once (all threads load lse values side by side) and kept in LDS; then
+// thread t sums w_s out_s[d] over the splits s = t / D (mod NT / D) for
+// d = t % D, four independent partial sums deep, and the NT / D parts are
+// added through LDS.  The loads are latency-bound, not bandwidth-bound, so
+// what matters is how many are in flight at once.
 template <int D>
 __global__ __launch_bounds__(NT) void splitkv_merge_kernel(const float* opart, const float* lpart, uint16_t* out,
                                                              float* lse, int64_t rows, int nsplit) {
-    const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
-    if (idx >= rows * D) return;
-    const int64_t row = idx / D;
-    const int d = (int)(idx % D);
+    constexpr int P = NT / D;  // parts per d
+    __shared__ float wsh[kMaxMergeSplits];
+    __shared__ float red[NT];
+    __shared__ float scratch[NT / 64];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lpart[s * rows + row]);
-    float Ls = 0.f, o = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float w = M == -INFINITY ? 0.f : __expf(lpart[s * rows + row] - M);
-        Ls += w;
-        o += w * opart[(s * rows + row) * D + d];
+    for (int s = tid; s < nsplit; s += NT) M = fmaxf(M, lpart[(int64_t)s * rows + row]);
+    M = block_reduce(M, true, scratch);
+    float Lpart = 0.f;
+    for (int s = tid; s < nsplit; s += NT) {
+        const float w = M == -INFINITY ? 0.f : __expf(lpart[(int64_t)s * rows + row] - M);
+        wsh[s] = w;
+        Lpart += w;
     }
-    const float v = Ls > 0.f ? o / Ls : 0.f;
-    out[idx] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
-    if (lse && d == 0) lse[row] = Ls > 0.f ? M + __logf(Ls) : -INFINITY;
+    const float Ls = block_reduce(Lpart, false, scratch);  // its barriers also publish wsh
+    const int d = tid % D, part = tid / D;
+    const float* base = opart + row * D + d;
+    const int64_t step = rows * D;  // one split further
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    int s = part;
+    for (; s + 3 * P < nsplit; s += 4 * P) {
+        o0 += wsh[s] * base[(int64_t)s * step];
+        o1 += wsh[s + P] * base[(int64_t)(s + P) * step];
+        o2 += wsh[s + 2 * P] * base[(int64_t)(s + 2 * P) * step];
+        o3 += wsh[s + 3 * P] * base[(int64_t)(s + 3 * P) * step];
+    }
+    for (; s < nsplit; s += P) o0 += wsh[s] * base[(int64_t)s * step];
+    red[tid] = (o0 + o1) + (o2 + o3);
+    __syncthreads();
+    if (part == 0) {
+        float o = red[d];
+#pragma unroll
+        for (int j = 1; j < P; ++j) o += red[d + j * D];
+        const float v = Ls > 0.f ? o / Ls : 0.f;
+        out[row * D + d] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
+        if (lse && d == 0) lse[row] = Ls > 0.f ? M + __logf(Ls) : -INFINITY;
+    }
 }
 
 template <typename K, typename P>
@@ -262,7 +319,7 @@ hipError_t launch_splitkv_bf16(const SplitKvArgs& a, hipStream_t stream) {
     hipError_t e = a.D == 128 ? launch1(&splitkv_bf16_kernel<128>, prm.total, prm, stream)
                               : launch1(&splitkv_bf16_kernel<64>, prm.total, prm, stream);
     if (e != hipSuccess) return e;
-    const uint32_t mgrid = (uint32_t)((rows * a.D + NT - 1) / NT);
+    const uint32_t mgrid = (uint32_t)rows;  // one workgroup per row
     const float* op = prm.opart;
     const float* lp = prm.lpart;
     uint16_t* out = (uint16_t*)a.out;
