@@ -146,3 +146,22 @@ def test_long_sequence_sampled(orc):
     ref_o, ref_l = orc.attn_fwd_blockmask(q.f32, k.f32, v.f32, sc, False, m, rows=rows)
     idx = torch.from_numpy(rows).to(out.device)
     check_masked(f"S=40000 blockmask rows={rows.size}", out.view(-1, D)[idx], lse.view(-1)[idx], ref_o, ref_l, D)
+
+
+def test_max_sequence(orc):
+    """S = 131072, the block mask's limit: 2048 key tiles, the longest list a
+    workgroup can hold (causal, so late workgroups list up to all of them)."""
+    B, Hq, Hkv, S, D = 1, 1, 1, 131072, 64
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", seed=7500)
+    nb = nblk(S)
+    rng = np.random.default_rng(7501)
+    m = (rng.random((1, 1, nb, nb)) < 0.05).astype(np.uint8)
+    m[0, 0, -1, :] = 1  # the last query block lists every tile
+    np.fill_diagonal(m[0, 0], 1)
+    sc = 1.0 / math.sqrt(D)
+    out, lse = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=True, scale=sc, block_mask=torch.from_numpy(m).cuda())
+    torch.cuda.synchronize()
+    rows = G.sample_rows(B, Hq, S, n_random=30, seed=7502, tile=256)
+    ref_o, ref_l = orc.attn_fwd_blockmask(q.f32, k.f32, v.f32, sc, True, m, rows=rows)
+    idx = torch.from_numpy(rows).to(out.device)
+    check_masked(f"S=131072 blockmask rows={rows.size}", out.view(-1, D)[idx], lse.view(-1)[idx], ref_o, ref_l, D)

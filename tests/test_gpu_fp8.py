@@ -104,6 +104,19 @@ def test_moving_reference(orc, shape, step, causal):
     check_fp8(orc, f"fp8 ramp {step:+g} {shape} causal={causal}", q, k, v, causal, out, lse)
 
 
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_long_sequence_sampled(orc, causal):
+    """S = 32768: the weights' reference keeps moving over 512 key tiles."""
+    B, Hq, Hkv, S, D = 1, 2, 1, 32768, 128
+    q, k, v = inputs.make_qkv_fp8(B, Hq, Hkv, S, D, seed=6300)
+    out, lse = api.fwd_fp8(codes(q), codes(k), codes(v), q.scale, k.scale, v.scale, causal=causal)
+    torch.cuda.synchronize()
+    rows = G.sample_rows(B, Hq, S, n_random=40, seed=6301, tile=256)
+    idx = torch.from_numpy(rows).to(out.device)
+    check_fp8(orc, f"fp8 S=32768 causal={causal} rows={rows.size}", q, k, v, causal, out.view(-1, D)[idx],
+              lse.view(-1)[idx], rows=rows)
+
+
 def test_gqa_and_row0():
     """Causal row 0 sees key 0 only: its one weight w cancels in w v / w, so
     out = v_0 * v_scale rounded to bf16, for every head of a GQA group."""

@@ -88,6 +88,22 @@ def test_config(orc, name, causal):
         assert torch.equal(out[:, :, 0, :], v0)
 
 
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_long_sequence(orc, causal):
+    """S = 65536 (1024 key tiles, 256 query workgroups per head) on sampled
+    rows, including the last rows of the sequence."""
+    B, Hq, Hkv, S, D = 1, 2, 1, 65536, 128
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", seed=90)
+    sc = 1.0 / math.sqrt(D)
+    out, lse = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    rows = G.sample_rows(B, Hq, S, n_random=40, seed=91, tile=256)
+    ref_o, ref_l = orc.attn_fwd(q.f32, k.f32, v.f32, sc, causal, rows=rows)
+    idx = torch.from_numpy(rows).to(out.device)
+    G.check_close(f"S=65536 causal={causal} rows={rows.size}", G.host(out.view(-1, D)[idx]), ref_o, "bf16",
+                  G.host(lse.view(-1)[idx]), ref_l)
+
+
 def test_row0_bitwise_f32():
     q, k, v = inputs.make_qkv(2, 4, 2, 70, 64, "f32", seed=77)
     out, _ = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=True)
