@@ -19,8 +19,9 @@
 //   bwd_dkdv_kernel    a workgroup owns 128 keys of one key/value head and
 //                      sweeps every query (of every query head of its group)
 //                      that sees them: S = Q K^T and dP = dO V^T with K, V in
-//                      registers, then dV^T += dO^T P and dK^T += Q^T dS with
-//                      Q and dO read transposed from LDS.
+//                      LDS, then dV^T += dO^T P and dK^T += Q^T dS with Q and
+//                      dO read transposed from LDS; two waves share each
+//                      32-key column block, one per half of a query tile.
 //   bwd_dq_kernel      a workgroup owns 128 queries and sweeps their keys:
 //                      S^T = K Q^T and dP^T = V dO^T with Q, dO in
 //                      registers, then dQ^T += K^T dS^T with K read
@@ -42,7 +43,7 @@
 namespace attn {
 namespace {
 
-constexpr int NT = 256;       // 4 waves
+constexpr int NT = 256;       // 4 waves (delta, dQ)
 constexpr int KEYS_WG = 128;  // keys per dK/dV workgroup (32 per wave)
 constexpr int QRY_TILE = 64;  // queries per step of the dK/dV sweep
 constexpr int QRY_WG = 128;   // queries per dQ workgroup (32 per wave)
@@ -94,46 +95,59 @@ __global__ __launch_bounds__(NT) void bwd_delta_kernel(BwdParams p, int64_t rows
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  Workgroup = (b, kv head g, 128-key tile); wave w owns keys
-// n0 + 32w .. +31 (lane l32 = key).  Sweeps the query heads of the group and
-// their 64-query tiles from the first one that sees the keys.
+// dK, dV.  Workgroup = (b, kv head g, 128-key tile) of 8 waves, two per SIMD;
+// waves w and w + 4 own keys n0 + 32 (w % 4) .. +31 (lane l32 = key) and take
+// the first and second 32 queries of every 64-query tile.  The workgroup
+// sweeps the query heads of the group and their 64-query tiles from the first
+// one that sees the keys.  K and V of the workgroup's keys stay in LDS (the
+// B operands of S = Q K^T and dP = dO V^T are read from there), which keeps
+// each wave, with its dK^T and dV^T accumulators, within 256 registers; at
+// one wave per SIMD with K and V in registers (392 registers) the products
+// and the exponentials of a wave could not overlap.  At the end waves 4-7
+// add their partial dK^T, dV^T into waves 0-3 through LDS.
 // ---------------------------------------------------------------------------
+constexpr int NT2 = 512;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(NT2) void bwd_dkdv_kernel(BwdParams p) {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    using TQ = RowTile<D, QRY_TILE, NT>;
+    using TQ = RowTile<D, QRY_TILE, NT2>;
+    using TK = RowTile<D, KEYS_WG, NT2>;
+    __shared__ __attribute__((aligned(16))) uint16_t KVs[2 * KEYS_WG * D];  // K rows, then V rows
     __shared__ __attribute__((aligned(16))) uint16_t Qs[QRY_TILE * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Os[QRY_TILE * D];  // dout tile
-    __shared__ __attribute__((aligned(16))) float Ls[QRY_TILE];        // lse * log2(e); +inf past S
-    __shared__ __attribute__((aligned(16))) float Ds[QRY_TILE];        // delta
+    __shared__ __attribute__((aligned(16))) uint16_t Os[QRY_TILE * D];      // dout tile
+    __shared__ __attribute__((aligned(16))) float Ls[QRY_TILE];             // lse * log2(e); +inf past S
+    __shared__ __attribute__((aligned(16))) float Ds[QRY_TILE];             // delta
+    uint16_t* Ks = KVs;
+    uint16_t* Vs = KVs + KEYS_WG * D;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g = lane >> 5;
+    const int kq = wave & 3;   // key quarter of the workgroup
+    const int xh = wave >> 2;  // which 32 queries of each 64-query tile
     const uint32_t L = xcd_remap(blockIdx.x, p.total);
     const int bg = (int)(L / (uint32_t)p.ntiles);
     const int tile = (int)(L % (uint32_t)p.ntiles);  // ascending: longest sweeps first under the mask
     const int b = bg / p.Hkv, kvh = bg % p.Hkv;
     const int S = p.S;
     const int n0 = tile * KEYS_WG;
-    const int key = n0 + wave * 32 + l32;
+    const int key = n0 + kq * 32 + l32;
     const uint16_t* kb = p.k + (int64_t)bg * S * D;
     const uint16_t* vb = p.v + (int64_t)bg * S * D;
-
-    bf16x8 kreg[KS], vreg[KS];  // B operands: column = this lane's key, k = d
+    {
+        TK tk, tv;
+        tk.load(kb, n0, S, tid);  // rows past S are zero
+        tv.load(vb, n0, S, tid);
+        tk.store(Ks, tid);
+        tv.store(Vs, tid);
+    }
+    int roff[KS], koff[KS];  // row l32 of this wave's query block / key quarter, chunk 2ks + g
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        u32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
-        if (key < S) {
-            a = *(const u32x4*)(kb + (int64_t)key * D + ks * 16 + g * 8);
-            c = *(const u32x4*)(vb + (int64_t)key * D + ks * 16 + g * 8);
-        }
-        kreg[ks] = as_bf16x8(a);
-        vreg[ks] = as_bf16x8(c);
+        roff[ks] = SwzTile<D>::at(xh * 32 + l32, (2 * ks + g) * 8);
+        koff[ks] = SwzTile<D>::at(kq * 32 + l32, (2 * ks + g) * 8);
     }
-    int roff[KS];  // row read of row l32, chunk 2ks + g
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) roff[ks] = SwzTile<D>::at(l32, (2 * ks + g) * 8);
     TrOffsets<D> tr;
     tr.init(lane);
 
@@ -164,7 +178,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdParams p) {
     if (steps > 0) fetch(0);
     for (int s = 0; s < steps; ++s) {
         const int m0 = (qt0 + s % (nqt - qt0)) * QRY_TILE;
-        __syncthreads();  // previous tile consumed
+        __syncthreads();  // previous tile consumed (and, at s = 0, K and V stored)
         tq.store(Qs, tid);
         to.store(Os, tid);
         if (tid < QRY_TILE) {
@@ -173,49 +187,71 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdParams p) {
         }
         __syncthreads();
         if (s + 1 < steps) fetch(s + 1);
+        const int qb = m0 + xh * 32;  // first query of this wave's block
+        // every query of the block is before every key of the wave: nothing visible
+        if (CAUSAL && qb + 31 < n0 + kq * 32) continue;
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-        for (int xb = 0; xb < 2; ++xb) {
-            const int qb = m0 + xb * 32;  // first query of this 32-query block
-            // every query of the block is before every key of the wave: nothing visible
-            if (CAUSAL && qb + 31 < n0 + wave * 32) continue;
-            f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 aq = *(const bf16x8*)(Qs + roff[ks]);
+            const bf16x8 ao = *(const bf16x8*)(Os + roff[ks]);
+            const bf16x8 bk = *(const bf16x8*)(Ks + koff[ks]);
+            const bf16x8 bv = *(const bf16x8*)(Vs + koff[ks]);
+            sacc = mfma32x32x16(aq, bk, sacc);
+            dpacc = mfma32x32x16(ao, bv, dpacc);
+        }
+        // row r of the accumulators: query qb + 8(r/4) + 4g + r%4
+        f32x16 pv, dsv;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 aq = *(const bf16x8*)(Qs + xb * 32 * D + roff[ks]);
-                const bf16x8 ao = *(const bf16x8*)(Os + xb * 32 * D + roff[ks]);
-                sacc = mfma32x32x16(aq, kreg[ks], sacc);
-                dpacc = mfma32x32x16(ao, vreg[ks], dpacc);
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int rl = xh * 32 + q4 * 8 + g * 4;
+            const f32x4 l4 = *(const f32x4*)(Ls + rl);
+            const f32x4 d4 = *(const f32x4*)(Ds + rl);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = q4 * 4 + e;
+                float pr = fast_exp2(fmaf(sacc[r], c, -l4[e]));
+                if (CAUSAL && key > m0 + rl + e) pr = 0.f;
+                pv[r] = pr;
+                dsv[r] = pr * (dpacc[r] - d4[e]);
             }
-            // row r of the accumulators: query qb + 8(r/4) + 4g + r%4
-            f32x16 pv, dsv;
+        }
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int rl = xb * 32 + q4 * 8 + g * 4;
-                const f32x4 l4 = *(const f32x4*)(Ls + rl);
-                const f32x4 d4 = *(const f32x4*)(Ds + rl);
+        for (int half = 0; half < 2; ++half) {
+            const bf16x8 pb = pack8(pv, half);
+            const bf16x8 db8 = pack8(dsv, half);
+            const int kblk = xh * 2 + half;  // 16-query block of the tile
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = q4 * 4 + e;
-                    float pr = fast_exp2(fmaf(sacc[r], c, -l4[e]));
-                    if (CAUSAL && key > m0 + rl + e) pr = 0.f;
-                    pv[r] = pr;
-                    dsv[r] = pr * (dpacc[r] - d4[e]);
-                }
-            }
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const bf16x8 pb = pack8(pv, half);
-                const bf16x8 db8 = pack8(dsv, half);
-                const int kblk = xb * 2 + half;  // 16-query block of the tile
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    dvacc[db] = mfma32x32x16(tr.read(Os, kblk, db), pb, dvacc[db]);
-                    dkacc[db] = mfma32x32x16(tr.read(Qs, kblk, db), db8, dkacc[db]);
-                }
+            for (int db = 0; db < DB; ++db) {
+                dvacc[db] = mfma32x32x16(tr.read(Os, kblk, db), pb, dvacc[db]);
+                dkacc[db] = mfma32x32x16(tr.read(Qs, kblk, db), db8, dkacc[db]);
             }
         }
     }
-    if (key < S) {
+
+    // waves 4-7 hand their partial sums to waves 0-3: dV^T, then dK^T,
+    // through the K/V area (4 waves x DB x 16 x 64 floats = 32 KB at D = 128)
+    float* red = (float*)KVs;
+    static_assert(4 * DB * 16 * 64 * 4 <= 2 * KEYS_WG * D * 2, "reduction area fits");
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        f32x16* acc = pass == 0 ? dvacc : dkacc;
+        __syncthreads();  // last reads of the area done
+        if (xh == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) red[((kq * DB + db) * 16 + e) * 64 + lane] = acc[db][e];
+        }
+        __syncthreads();
+        if (xh == 0) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[db][e] += red[((kq * DB + db) * 16 + e) * 64 + lane];
+        }
+    }
+    if (xh == 0 && key < S) {
         uint16_t* dkr = p.dk + ((int64_t)bg * S + key) * D;
         uint16_t* dvr = p.dv + ((int64_t)bg * S + key) * D;
         const float sc = p.scale;
@@ -345,10 +381,10 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
 }
 
 template <typename K>
-hipError_t launch(K kernel, uint32_t grid, const BwdParams& prm, hipStream_t stream) {
+hipError_t launch(K kernel, uint32_t grid, const BwdParams& prm, hipStream_t stream, int threads = NT) {
     BwdParams arg = prm;
     void* args[] = {&arg};
-    return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(NT), args, 0, stream);
+    return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(threads), args, 0, stream);
 }
 
 template <typename K>
@@ -366,8 +402,8 @@ hipError_t run(BwdParams prm, const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     prm.ntiles = (a.S + KEYS_WG - 1) / KEYS_WG;
     prm.total = (uint32_t)((int64_t)a.B * a.Hkv * prm.ntiles);
-    e = a.causal ? launch(&bwd_dkdv_kernel<D, true>, prm.total, prm, stream)
-                 : launch(&bwd_dkdv_kernel<D, false>, prm.total, prm, stream);
+    e = a.causal ? launch(&bwd_dkdv_kernel<D, true>, prm.total, prm, stream, NT2)
+                 : launch(&bwd_dkdv_kernel<D, false>, prm.total, prm, stream, NT2);
     if (e != hipSuccess) return e;
     prm.ntiles = (a.S + QRY_WG - 1) / QRY_WG;
     prm.total = (uint32_t)((int64_t)a.B * a.Hq * prm.ntiles);
