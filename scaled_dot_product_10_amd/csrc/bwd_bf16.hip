@@ -38,6 +38,7 @@
 // LDS read provides.
 #include "common.h"
 #include "launch.h"
+#include "lds_dma.h"
 #include "lds_tiles.h"
 
 namespace attn {
@@ -271,19 +272,54 @@ __global__ __launch_bounds__(NT2) void bwd_dkdv_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dQ.  Workgroup = (b, h, 128-query tile), longest (last) tiles first; wave w
-// owns queries m0 + 32w .. +31 (lane l32 = query).  Sweeps 64-key tiles.
+// owns queries m0 + 32w .. +31 (lane l32 = query).  Sweeps 64-key tiles,
+// which reach LDS by global_load_lds_dwordx4 (no register staging) into two
+// buffers: tile t+1 is in flight while tile t is multiplied, with one
+// barrier per tile.
 // ---------------------------------------------------------------------------
 // At most 256 registers, so two waves share each SIMD (measured 16% faster
 // overall than one wave per SIMD).
+
+// DMA of one 64-row K or V tile into a SwzTile: instruction i of wave w fills
+// LDS chunk positions p = (w PER + i) 64 + lane, i.e. row p / CPR at chunk
+// position p % CPR, which holds chunk (p % CPR) ^ swz(row); rows past the
+// end of the sequence repeat row S-1 (those keys are masked).
+template <int D>
+struct SwzDma {
+    static constexpr int CPR = D / 8;
+    static constexpr int PER = KEY_TILE * CPR / 64 / (NT / 64);  // instructions per wave
+    uint32_t off[PER];
+    __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int pos = (wave * PER + i) * 64 + lane;
+            const int r = pos / CPR;
+            off[i] = (uint32_t)(r * D * 2 + (((pos % CPR) ^ SwzTile<D>::swz(r)) * 16));
+        }
+    }
+    __device__ __forceinline__ void issue(const uint16_t* base, int n0, int S, uint16_t* tile, int wave) const {
+        const uint16_t* tb = base + (int64_t)n0 * D;
+        const uint32_t l0 = lds_addr(tile) + (uint32_t)(wave * PER) * 1024u;
+        const int last = S - 1 - n0;  // last valid row of this tile
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int r = (int)(off[i] / (D * 2));
+            const uint32_t o = n0 + KEY_TILE <= S ? off[i] : off[i] - (uint32_t)((r - min(r, last)) * D * 2);
+            dma16(tb, o, l0 + i * 1024);
+        }
+    }
+};
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    using TK = RowTile<D, KEY_TILE, NT>;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KEY_TILE * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[KEY_TILE * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t KVs[4 * KEY_TILE * D];  // K(buf 0), K(buf 1), V(0), V(1)
+    auto Kbuf = [&](int t) __attribute__((always_inline)) { return KVs + (t & 1) * KEY_TILE * D; };
+    auto Vbuf = [&](int t) __attribute__((always_inline)) { return KVs + (2 + (t & 1)) * KEY_TILE * D; };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the DMA's LDS address is scalar
     const int l32 = lane & 31, g = lane >> 5;
     const uint32_t L = xcd_remap(blockIdx.x, p.total);
     const int bh = (int)(L / (uint32_t)p.ntiles);
@@ -323,19 +359,21 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
     const int qlast = min(m0 + QRY_WG, S) - 1;
     const int nkt = CAUSAL ? qlast / KEY_TILE + 1 : (S + KEY_TILE - 1) / KEY_TILE;
     const float c = p.c;
-    TK tk, tv;
-    tk.load(kb, 0, S, tid);
-    tv.load(vb, 0, S, tid);
+    SwzDma<D> dma;
+    dma.init(wave, lane);
+    dma.issue(kb, 0, S, Kbuf(0), wave);
+    dma.issue(vb, 0, S, Vbuf(0), wave);
     for (int t = 0; t < nkt; ++t) {
         const int k0 = t * KEY_TILE;
-        __syncthreads();
-        tk.store(Ks, tid);
-        tv.store(Vs, tid);
-        __syncthreads();
+        // tile t has landed for every wave, and every wave is done with the
+        // buffers of tile t-1, which tile t+1 now fills
+        phase_barrier(true);
         if (t + 1 < nkt) {
-            tk.load(kb, k0 + KEY_TILE, S, tid);
-            tv.load(vb, k0 + KEY_TILE, S, tid);
+            dma.issue(kb, k0 + KEY_TILE, S, Kbuf(t + 1), wave);
+            dma.issue(vb, k0 + KEY_TILE, S, Vbuf(t + 1), wave);
         }
+        const uint16_t* Ks = Kbuf(t);
+        const uint16_t* Vs = Vbuf(t);
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int kb0 = k0 + sb * 32;

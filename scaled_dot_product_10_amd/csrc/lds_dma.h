@@ -1,5 +1,5 @@
-// Tile DMA into LDS and the phase barrier shared by the two-group kernels
-// (fused forward bf16 and fp8, backward dQ).
+// Tile DMA into LDS and the barrier that publishes a tile, shared by the fused
+// forward kernels (bf16, fp8) and the backward dQ sweep.
 #pragma once
 
 #include "common.h"
