@@ -95,6 +95,38 @@ __global__ __launch_bounds__(NT) void bwd_delta_kernel(BwdParams p, int64_t rows
     if (row < rows && tid % LPR == 0) p.delta[row] = acc;
 }
 
+// DMA of one 64-row tile (K, V, Q or dO) into a SwzTile by NW waves: instruction i of wave w fills
+// LDS chunk positions p = (w PER + i) 64 + lane, i.e. row p / CPR at chunk
+// position p % CPR, which holds chunk (p % CPR) ^ swz(row); rows past the
+// end of the sequence repeat row S-1 (those keys are masked, those queries
+// have lse = +inf and weight 0).
+template <int D, int NW>
+struct SwzDma {
+    static constexpr int CPR = D / 8;
+    static constexpr int PER = 64 * CPR / 64 / NW;  // instructions per wave
+    static_assert(PER >= 1 && PER * NW * 64 == 64 * CPR, "whole tile, whole instructions");
+    uint32_t off[PER];
+    __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int pos = (wave * PER + i) * 64 + lane;
+            const int r = pos / CPR;
+            off[i] = (uint32_t)(r * D * 2 + (((pos % CPR) ^ SwzTile<D>::swz(r)) * 16));
+        }
+    }
+    __device__ __forceinline__ void issue(const uint16_t* base, int n0, int S, uint16_t* tile, int wave) const {
+        const uint16_t* tb = base + (int64_t)n0 * D;
+        const uint32_t l0 = lds_addr(tile) + (uint32_t)(wave * PER) * 1024u;
+        const int last = S - 1 - n0;  // last valid row of this tile
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int r = (int)(off[i] / (D * 2));
+            const uint32_t o = n0 + 64 <= S ? off[i] : off[i] - (uint32_t)((r - min(r, last)) * D * 2);
+            dma16(tb, o, l0 + i * 1024);
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------
 // dK, dV.  Workgroup = (b, kv head g, 128-key tile) of 8 waves, two per SIMD;
 // waves w and w + 4 own keys n0 + 32 (w % 4) .. +31 (lane l32 = key) and take
@@ -113,17 +145,16 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NT2) void bwd_dkdv_kernel(BwdParams p) {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    using TQ = RowTile<D, QRY_TILE, NT2>;
     using TK = RowTile<D, KEYS_WG, NT2>;
-    __shared__ __attribute__((aligned(16))) uint16_t KVs[2 * KEYS_WG * D];  // K rows, then V rows
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[QRY_TILE * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Os[QRY_TILE * D];      // dout tile
-    __shared__ __attribute__((aligned(16))) float Ls[QRY_TILE];             // lse * log2(e); +inf past S
-    __shared__ __attribute__((aligned(16))) float Ds[QRY_TILE];             // delta
+    static_assert(QRY_TILE == 64, "one SwzDma tile per query tile");
+    __shared__ __attribute__((aligned(1024))) uint16_t KVs[2 * KEYS_WG * D];   // K rows, then V rows
+    __shared__ __attribute__((aligned(1024))) uint16_t QOs[4 * QRY_TILE * D];  // Q(buf 0), Q(1), dO(0), dO(1)
+    __shared__ __attribute__((aligned(16))) float LDs[2][2][QRY_TILE];         // [buf]: lse * log2(e) (+inf past S), delta
     uint16_t* Ks = KVs;
     uint16_t* Vs = KVs + KEYS_WG * D;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the DMA's LDS address is scalar
     const int l32 = lane & 31, g = lane >> 5;
     const int kq = wave & 3;   // key quarter of the workgroup
     const int xh = wave >> 2;  // which 32 queries of each 64-query tile
@@ -162,78 +193,96 @@ __global__ __launch_bounds__(NT2) void bwd_dkdv_kernel(BwdParams p) {
     const float c = p.c;
     const float kLog2eF = kLog2e;
 
-    TQ tq, to;
+    // Q, dO tiles by DMA into two buffers; lse and delta of the next tile go
+    // through registers and are stored after the current tile's products
+    SwzDma<D, NT2 / 64> dma;
+    dma.init(wave, lane);
     float lnext = 0.f, dnext = 0.f;
-    auto fetch = [&](int s) __attribute__((always_inline)) {
+    auto fetch = [&](int s, int buf) __attribute__((always_inline)) {
         const int h = kvh * p.group + s / (nqt - qt0);
         const int m0 = (qt0 + s % (nqt - qt0)) * QRY_TILE;
         const int64_t rowb = ((int64_t)b * p.Hq + h) * S;
-        tq.load(p.q + rowb * D, m0, S, tid);
-        to.load(p.dout + rowb * D, m0, S, tid);
+        dma.issue(p.q + rowb * D, m0, S, QOs + buf * QRY_TILE * D, wave);
+        dma.issue(p.dout + rowb * D, m0, S, QOs + (2 + buf) * QRY_TILE * D, wave);
         if (tid < QRY_TILE) {
             const int i = m0 + tid;
             lnext = i < S ? p.lse[rowb + i] * kLog2eF : INFINITY;
             dnext = i < S ? p.delta[rowb + i] : 0.f;
         }
     };
-    if (steps > 0) fetch(0);
+    if (steps > 0) {
+        fetch(0, 0);
+        if (tid < QRY_TILE) {
+            LDs[0][0][tid] = lnext;
+            LDs[0][1][tid] = dnext;
+        }
+    }
     for (int s = 0; s < steps; ++s) {
         const int m0 = (qt0 + s % (nqt - qt0)) * QRY_TILE;
-        __syncthreads();  // previous tile consumed (and, at s = 0, K and V stored)
-        tq.store(Qs, tid);
-        to.store(Os, tid);
-        if (tid < QRY_TILE) {
-            Ls[tid] = lnext;
-            Ds[tid] = dnext;
-        }
-        __syncthreads();
-        if (s + 1 < steps) fetch(s + 1);
+        const int buf = s & 1;
+        // tile s has landed for every wave (and, at s = 0, K and V are
+        // stored); every wave is done with buffer buf ^ 1 (tile s - 1)
+        phase_barrier(true);
+        if (s + 1 < steps) fetch(s + 1, buf ^ 1);
+        const uint16_t* Qs = QOs + buf * QRY_TILE * D;
+        const uint16_t* Os = QOs + (2 + buf) * QRY_TILE * D;
+        const float* Ls = LDs[buf][0];
+        const float* Ds = LDs[buf][1];
+        auto publish_next = [&]() __attribute__((always_inline)) {
+            if (s + 1 < steps && tid < QRY_TILE) {
+                LDs[buf ^ 1][0][tid] = lnext;
+                LDs[buf ^ 1][1][tid] = dnext;
+            }
+        };
         const int qb = m0 + xh * 32;  // first query of this wave's block
-        // every query of the block is before every key of the wave: nothing visible
-        if (CAUSAL && qb + 31 < n0 + kq * 32) continue;
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        // unless every query of the block is before every key of the wave
+        if (!CAUSAL || qb + 31 >= n0 + kq * 32) {
+            f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 aq = *(const bf16x8*)(Qs + roff[ks]);
-            const bf16x8 ao = *(const bf16x8*)(Os + roff[ks]);
-            const bf16x8 bk = *(const bf16x8*)(Ks + koff[ks]);
-            const bf16x8 bv = *(const bf16x8*)(Vs + koff[ks]);
-            sacc = mfma32x32x16(aq, bk, sacc);
-            dpacc = mfma32x32x16(ao, bv, dpacc);
-        }
-        // row r of the accumulators: query qb + 8(r/4) + 4g + r%4
-        f32x16 pv, dsv;
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 aq = *(const bf16x8*)(Qs + roff[ks]);
+                const bf16x8 ao = *(const bf16x8*)(Os + roff[ks]);
+                const bf16x8 bk = *(const bf16x8*)(Ks + koff[ks]);
+                const bf16x8 bv = *(const bf16x8*)(Vs + koff[ks]);
+                sacc = mfma32x32x16(aq, bk, sacc);
+                dpacc = mfma32x32x16(ao, bv, dpacc);
+            }
+            // row r of the accumulators: query qb + 8(r/4) + 4g + r%4
+            f32x16 pv, dsv;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int rl = xh * 32 + q4 * 8 + g * 4;
-            const f32x4 l4 = *(const f32x4*)(Ls + rl);
-            const f32x4 d4 = *(const f32x4*)(Ds + rl);
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int rl = xh * 32 + q4 * 8 + g * 4;
+                const f32x4 l4 = *(const f32x4*)(Ls + rl);
+                const f32x4 d4 = *(const f32x4*)(Ds + rl);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = q4 * 4 + e;
-                float pr = fast_exp2(fmaf(sacc[r], c, -l4[e]));
-                if (CAUSAL && key > m0 + rl + e) pr = 0.f;
-                pv[r] = pr;
-                dsv[r] = pr * (dpacc[r] - d4[e]);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = q4 * 4 + e;
+                    float pr = fast_exp2(fmaf(sacc[r], c, -l4[e]));
+                    if (CAUSAL && key > m0 + rl + e) pr = 0.f;
+                    pv[r] = pr;
+                    dsv[r] = pr * (dpacc[r] - d4[e]);
+                }
+            }
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const bf16x8 pb = pack8(pv, half);
+                const bf16x8 db8 = pack8(dsv, half);
+                const int kblk = xh * 2 + half;  // 16-query block of the tile
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dvacc[db] = mfma32x32x16(tr.read(Os, kblk, db), pb, dvacc[db]);
+                    dkacc[db] = mfma32x32x16(tr.read(Qs, kblk, db), db8, dkacc[db]);
+                }
             }
         }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const bf16x8 pb = pack8(pv, half);
-            const bf16x8 db8 = pack8(dsv, half);
-            const int kblk = xh * 2 + half;  // 16-query block of the tile
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                dvacc[db] = mfma32x32x16(tr.read(Os, kblk, db), pb, dvacc[db]);
-                dkacc[db] = mfma32x32x16(tr.read(Qs, kblk, db), db8, dkacc[db]);
-            }
-        }
+        publish_next();
     }
 
     // waves 4-7 hand their partial sums to waves 0-3: dV^T, then dK^T,
     // through the K/V area (4 waves x DB x 16 x 64 floats = 32 KB at D = 128)
     float* red = (float*)KVs;
     static_assert(4 * DB * 16 * 64 * 4 <= 2 * KEYS_WG * D * 2, "reduction area fits");
+    // (the last tile's K/V reads end before the first barrier below)
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
         f32x16* acc = pass == 0 ? dvacc : dkacc;
@@ -279,36 +328,6 @@ __global__ __launch_bounds__(NT2) void bwd_dkdv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // At most 256 registers, so two waves share each SIMD (measured 16% faster
 // overall than one wave per SIMD).
-
-// DMA of one 64-row K or V tile into a SwzTile: instruction i of wave w fills
-// LDS chunk positions p = (w PER + i) 64 + lane, i.e. row p / CPR at chunk
-// position p % CPR, which holds chunk (p % CPR) ^ swz(row); rows past the
-// end of the sequence repeat row S-1 (those keys are masked).
-template <int D>
-struct SwzDma {
-    static constexpr int CPR = D / 8;
-    static constexpr int PER = KEY_TILE * CPR / 64 / (NT / 64);  // instructions per wave
-    uint32_t off[PER];
-    __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int pos = (wave * PER + i) * 64 + lane;
-            const int r = pos / CPR;
-            off[i] = (uint32_t)(r * D * 2 + (((pos % CPR) ^ SwzTile<D>::swz(r)) * 16));
-        }
-    }
-    __device__ __forceinline__ void issue(const uint16_t* base, int n0, int S, uint16_t* tile, int wave) const {
-        const uint16_t* tb = base + (int64_t)n0 * D;
-        const uint32_t l0 = lds_addr(tile) + (uint32_t)(wave * PER) * 1024u;
-        const int last = S - 1 - n0;  // last valid row of this tile
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int r = (int)(off[i] / (D * 2));
-            const uint32_t o = n0 + KEY_TILE <= S ? off[i] : off[i] - (uint32_t)((r - min(r, last)) * D * 2);
-            dma16(tb, o, l0 + i * 1024);
-        }
-    }
-};
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
@@ -359,7 +378,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
     const int qlast = min(m0 + QRY_WG, S) - 1;
     const int nkt = CAUSAL ? qlast / KEY_TILE + 1 : (S + KEY_TILE - 1) / KEY_TILE;
     const float c = p.c;
-    SwzDma<D> dma;
+    SwzDma<D, NT / 64> dma;
     dma.init(wave, lane);
     dma.issue(kb, 0, S, Kbuf(0), wave);
     dma.issue(vb, 0, S, Vbuf(0), wave);
