@@ -130,7 +130,9 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Params p) {
     using T = Tile8<D>;
     constexpr int KS = D / 64;  // k-steps of the Q.K^T product
     constexpr int DB = D / 32;  // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * T::BYTES];
+    // K and V buffers; after the last barrier, the output staging area
+    constexpr int SMEM = 4 * T::BYTES > NW * 32 * D * 2 ? 4 * T::BYTES : NW * 32 * D * 2;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
     auto Kbuf = [&](int i) __attribute__((always_inline)) { return smem + (i & 1) * T::BYTES; };
     auto Vbuf = [&](int i) __attribute__((always_inline)) { return smem + (2 + (i & 1)) * T::BYTES; };
 
@@ -388,21 +390,31 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Params p) {
         }
     }
 
-    if (qi < S) {
-        const float l = lacc[0];
-        const float inv = p.vs / l;
-        uint16_t* orow = p.out + (row0 + qi) * D;
+    // O through this wave's share of the (now idle) LDS, so that the stores
+    // cover whole rows of the wave's 32 contiguous output rows (as in the
+    // bf16 kernel)
+    const float l = lacc[0];
+    const float inv = p.vs / l;
+    constexpr int RB = D * 2;     // bytes per output row
+    constexpr int CPO = RB / 16;  // 16-byte chunks per row; chunk c of row r at c ^ (r % CPO)
+    uint8_t* stage = smem + wave * 32 * RB;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int d0 = db * 32 + j * 8 + g * 4;
-                *(u32x2*)(orow + d0) = u32x2{pack_bf16x2(oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv),
-                                             pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv)};
-            }
+        for (int j = 0; j < 4; ++j) {
+            const u32x2 w = {pack_bf16x2(oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv),
+                             pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv)};
+            const int c = db * 4 + j;  // d = 32 db + 8 j + 4 g .. +3
+            *(u32x2*)(stage + l32 * RB + ((c ^ (l32 % CPO)) * 16) + g * 8) = w;
         }
-        if (p.lse && g == 0) p.lse[row0 + qi] = (ma + __log2f(l) - kBias) * kLn2;
     }
+#pragma unroll
+    for (int i = 0; i < 32 * CPO / 64; ++i) {
+        const int pos = i * 64 + lane, r = pos / CPO, c = pos % CPO;
+        const u32x4 x = *(const u32x4*)(stage + r * RB + ((c ^ (r % CPO)) * 16));
+        if (qwmin + r < S) *(u32x4*)(p.out + (row0 + qwmin + r) * D + c * 8) = x;
+    }
+    if (qi < S && p.lse && g == 0) p.lse[row0 + qi] = (ma + __log2f(l) - kBias) * kLn2;
 }
 
 template <int D, bool CAUSAL>
