@@ -34,6 +34,7 @@
 #include "common.h"
 #include "launch.h"
 #include "lds_dma.h"
+#include "lds_tiles.h"
 
 namespace attn {
 namespace {
@@ -395,25 +396,7 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Params p) {
     // bf16 kernel)
     const float l = lacc[0];
     const float inv = p.vs / l;
-    constexpr int RB = D * 2;     // bytes per output row
-    constexpr int CPO = RB / 16;  // 16-byte chunks per row; chunk c of row r at c ^ (r % CPO)
-    uint8_t* stage = smem + wave * 32 * RB;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u32x2 w = {pack_bf16x2(oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv),
-                             pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv)};
-            const int c = db * 4 + j;  // d = 32 db + 8 j + 4 g .. +3
-            *(u32x2*)(stage + l32 * RB + ((c ^ (l32 % CPO)) * 16) + g * 8) = w;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 32 * CPO / 64; ++i) {
-        const int pos = i * 64 + lane, r = pos / CPO, c = pos % CPO;
-        const u32x4 x = *(const u32x4*)(stage + r * RB + ((c ^ (r % CPO)) * 16));
-        if (qwmin + r < S) *(u32x4*)(p.out + (row0 + qwmin + r) * D + c * 8) = x;
-    }
+    store_rows_via_lds<D>((char*)smem + wave * 32 * D * 2, oacc, inv, p.out + (row0 + qwmin) * D, S - qwmin, lane);
     if (qi < S && p.lse && g == 0) p.lse[row0 + qi] = (ma + __log2f(l) - kBias) * kLn2;
 }
 
