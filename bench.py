@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA (twice the bf16 rate)
 PROFILE = ROOT / "profiles" / "fwd_bf16_B4H16S4096D128_causal.md"
-KERNEL_SOURCES = ["fwd_bf16.hip", "common.h", "lds_dma.h"]
+KERNEL_SOURCES = ["fwd_bf16.hip", "common.h", "lds_dma.h", "lds_tiles.h"]
 
 
 def attn_flops(B, H, S, D, causal):
