@@ -80,15 +80,20 @@ struct TrOffsets {
 // acc[db] (lane l32 = output row, register 4j + e = column 32 db + 8 j + 4 g
 // + e), times the lane's scale, to bf16 rows dst + r D for r < nrows (the 32
 // rows are contiguous in memory).  Goes through 32 D 2 bytes of LDS owned by
-// the wave (chunk c of row r at c ^ (r % chunks per row)) so that every store
-// instruction writes whole rows, 16 bytes per lane: stores of 8 bytes per
-// lane spread over 32 rows cost several times more.
+// the wave so that every store instruction writes whole rows, 16 bytes per
+// lane: stores of 8 bytes per lane spread over 32 rows cost several times
+// more.  In LDS, 16-byte chunk c of row r sits at c ^ ((r / RPL) % CPO) (RPL
+// rows share one 256-byte bank line), with its two 8-byte halves swapped for
+// rows 16-31: the 32 lanes of one write (one row each, same chunk and half)
+// then cover all 64 banks once, and the reads (16 lanes per 256 bytes) too.
 template <int D>
 __device__ __forceinline__ void store_rows_via_lds(char* stage, const f32x16 (&acc)[D / 32], float scale,
                                                    uint16_t* dst, int nrows, int lane) {
     constexpr int RB = D * 2;     // bytes per row
     constexpr int CPO = RB / 16;  // 16-byte chunks per row
+    constexpr int RPL = 256 / RB; // rows per 256-byte bank line
     const int l32 = lane & 31, g = lane >> 5;
+    const int wswz = (l32 / RPL) % CPO, whalf = g ^ ((l32 >> 4) & 1);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -96,14 +101,15 @@ __device__ __forceinline__ void store_rows_via_lds(char* stage, const f32x16 (&a
             const u32x2 w = {pack_bf16x2(acc[db][4 * j] * scale, acc[db][4 * j + 1] * scale),
                              pack_bf16x2(acc[db][4 * j + 2] * scale, acc[db][4 * j + 3] * scale)};
             const int c = db * 4 + j;
-            *(u32x2*)(stage + l32 * RB + ((c ^ (l32 % CPO)) * 16) + g * 8) = w;
+            *(u32x2*)(stage + l32 * RB + ((c ^ wswz) * 16) + whalf * 8) = w;
         }
     }
     // the wave's own LDS writes complete before its reads (in order)
 #pragma unroll
     for (int i = 0; i < 32 * CPO / 64; ++i) {
         const int pos = i * 64 + lane, r = pos / CPO, c = pos % CPO;
-        const u32x4 x = *(const u32x4*)(stage + r * RB + ((c ^ (r % CPO)) * 16));
+        u32x4 x = *(const u32x4*)(stage + r * RB + ((c ^ ((r / RPL) % CPO)) * 16));
+        if ((r >> 4) & 1) x = u32x4{x[2], x[3], x[0], x[1]};
         if (r < nrows) *(u32x4*)(dst + (int64_t)r * D + c * 8) = x;
     }
 }
