@@ -8,21 +8,22 @@ import numpy as np
 
 # spec tolerances: max-abs / mean-abs error of out against the fp64 oracle
 TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}
-# lse is not bounded by the pages.  The bf16 kernels normalise by the sum of
-# the bf16-rounded weights they actually apply (so out is an exact convex
-# combination of v rows and lse matches out's normalisation); each rounded
-# weight is within 2^-8 of the exact one, relatively, so l is too and lse is
-# within ln(1 + 2^-8) < 3.9e-3 of the exact value, plus float32 rounding.
+# lse is not bounded by the pages.  The bf16 kernels normalise either by the
+# sum of the bf16-rounded weights they apply or (the fused forward) by the
+# float32 sum of the unrounded weights; each rounded weight is within a
+# relative 2^-8 (bf16's unit roundoff) of the exact one, so l is within that
+# of the exact sum either way and lse is within ln(1 + 2^-8) < 3.9e-3 of the
+# exact value, plus float32 rounding.
 LSE_TOL = {"bf16": 4e-3, "f32": 1e-5}
 
 
 # Backward gradients have no bound on the pages; errors are taken relative to
 # the size of the exact gradient (max |ref| for the max error, mean |ref| for
-# the mean error).  The bf16 kernels round p and ds to bf16 (relative 2^-9)
-# before the products that consume them and round dq, dk, dv to bf16
-# (relative 2^-9); float32 accumulates everything else.  Together that is
-# about 2^-8 = 3.9e-3 of the gradient's size at worst and half of it on
-# average (measured: at most 5.8e-3 and 2.7e-3 over the test shapes); the
+# the mean error).  The bf16 kernels round p and ds to bf16 (relative 2^-8 at
+# most, bf16's unit roundoff) before the products that consume them and round
+# dq, dk, dv to bf16 (the same); float32 accumulates everything else.  The
+# rounding errors have both signs and mostly cancel in the sums (measured: at
+# most 5.8e-3 and 2.7e-3 of the gradient's size over the test shapes); the
 # bounds leave a margin of about two.  A gradient that is
 # exactly zero (S = 1, causal query 0) is met only by the float32 rounding of
 # dp - delta, about D * 2^-24 * |dout| |v| ~ 1e-5 here, so the sizes are

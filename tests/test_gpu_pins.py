@@ -1,0 +1,183 @@
+"""Closed-form pins of the fused forward on the GPU (attn_fwd_bf16 / attn_fwd_f32).
+
+The same properties pin the oracle in test_oracle_pins.py; here they are
+checked on the HIP path directly, with expected values from the definition
+of softmax(q k^T * scale + mask) v (the Hugging Face article's naive
+attention, steps 1-5, and the plain formula Attention(Q, K, V) of the
+AttentionProfiler article), not from the oracle:
+  * q = 0: every logit is 0, so row i averages the rows of v it sees (the
+    running prefix mean under the causal mask, the mean of all rows without
+    it) and lse = ln(number of keys seen);
+  * identical keys: every logit of a row is equal, same averages, and
+    lse = scale q_i . kappa + ln(number of keys seen);
+  * out is linear in v: 2v gives exactly 2 out; v + 1 gives out + 1 up to the
+    normalisation (the weights applied are bf16-rounded, their sum is taken
+    in float32 from the unrounded weights: a relative 2^-8 at most);
+  * the last causal row sees every key, as does the last non-causal row;
+  * S = 1 returns v; causal row 0 returns v row 0 bit for bit;
+  * grouped-query heads equal multi-head attention with k, v repeated.
+Tolerances: bf16 keeps 8 significant bits, so rounding to nearest is within
+a relative u = 2^-8 (float32: 2^-24); weights of exactly 1 leave only the
+float32 sums and quotient (relative ~1e-6).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import gpu_util as G
+from scaled_dot_product_10_amd import api, inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+ROUND = {"bf16": 2.0 ** -8, "f32": 2.0 ** -24}  # unit roundoff of the output type
+SHAPES = [(1, 4, 2, 300, 128), (2, 2, 1, 129, 64)]  # ragged over 256-query and 64-key tiles
+
+
+def _prefix_mean(v64, causal):
+    """[B,H,S,D] float64: row i = mean of v rows 0..i (causal) or of all rows."""
+    S = v64.shape[2]
+    if causal:
+        return np.cumsum(v64, axis=2) / np.arange(1, S + 1, dtype=np.float64)[:, None]
+    return np.broadcast_to(v64.mean(axis=2, keepdims=True), v64.shape)
+
+
+def _check_mean(name, got, ref, dtype):
+    # one rounding of the output plus float32 sums of at most S terms
+    # (n 2^-24 of the largest partial sum, over n: below 1e-5 here)
+    tol = ROUND[dtype] * np.abs(ref) * 1.001 + 1e-5
+    err = np.abs(got - ref)
+    G.report(name, max_err=float(err.max()), max_excess=float((err - tol).max()))
+    assert np.all(err <= tol), f"{name}: max err {err.max():.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}H{}kv{}S{}D{}".format(*s))
+def test_zero_queries_average_v(shape, causal, dtype):
+    B, Hq, Hkv, S, D = shape
+    _, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, dtype, seed=301)
+    q = inputs._finish(np.zeros((B, Hq, S, D), np.float32), dtype)
+    out, lse = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=causal)
+    torch.cuda.synchronize()
+    v64 = np.repeat(v.f32.astype(np.float64), Hq // Hkv, axis=1)
+    _check_mean(f"q=0 {shape} causal={causal} {dtype}", G.host(out), _prefix_mean(v64, causal), dtype)
+    seen = np.arange(1, S + 1, dtype=np.float64) if causal else np.full(S, float(S))
+    lerr = np.abs(G.host(lse) - np.log(seen)).max()
+    assert lerr <= 1e-5, f"lse err {lerr:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}H{}kv{}S{}D{}".format(*s))
+def test_identical_keys_average_v(shape, causal, dtype):
+    B, Hq, Hkv, S, D = shape
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, dtype, seed=302)
+    kappa = k.f32[:, :, :1, :]
+    ks = inputs._finish(np.ascontiguousarray(np.broadcast_to(kappa, k.f32.shape)), dtype)
+    sc = 1.0 / math.sqrt(D)
+    out, lse = api.fwd(G.dev(q), G.dev(ks), G.dev(v), causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    g = Hq // Hkv
+    v64 = np.repeat(v.f32.astype(np.float64), g, axis=1)
+    _check_mean(f"k=kappa {shape} causal={causal} {dtype}", G.host(out), _prefix_mean(v64, causal), dtype)
+    kap = np.repeat(kappa.astype(np.float64), g, axis=1)  # [B,Hq,1,D]
+    dot = (q.f32.astype(np.float64) * kap).sum(-1)
+    seen = np.arange(1, S + 1, dtype=np.float64) if causal else np.full(S, float(S))
+    ref_l = sc * dot + np.log(seen)
+    # float32 dot products: gamma_D * scale * sum |q_d kappa_d|, plus exp2/log2
+    bound = D * 2.0 ** -24 * sc * (np.abs(q.f32.astype(np.float64)) * np.abs(kap)).sum(-1) + 1e-5
+    lerr = np.abs(G.host(lse) - ref_l)
+    assert np.all(lerr <= bound), f"lse err {lerr.max():.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_linear_in_v(causal, dtype):
+    B, Hq, Hkv, S, D = 1, 4, 2, 300, 128
+    q, k, _ = inputs.make_qkv(B, Hq, Hkv, S, D, dtype, seed=303)
+    rng = np.random.default_rng(303)
+    # v on a grid of 1/8 in [-4, 4]: v, 2v and v + 1 are exact in bf16
+    vg = np.clip(np.round(rng.standard_normal((B, Hkv, S, D)) * 8) / 8, -4, 4).astype(np.float32)
+    v, v2, v1 = (inputs._finish(x, dtype) for x in (vg, 2 * vg, vg + 1))
+    dq, dk = G.dev(q), G.dev(k)
+    o, _ = api.fwd(dq, dk, G.dev(v), causal=causal)
+    o2, _ = api.fwd(dq, dk, G.dev(v2), causal=causal)
+    o1, _ = api.fwd(dq, dk, G.dev(v1), causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, 2 * o), "out(2v) != 2 out(v)"  # scaling by 2 is exact at every step
+    a, o0 = G.host(o1), G.host(o)
+    b = o0 + 1.0
+    # the weights' sum differs from 1 by a relative u (bf16 weights) or by the
+    # float32 rounding of S-term sums (float32 path); each output is rounded
+    # once, within u of its own size
+    tol = ROUND[dtype] * (1.0 + np.abs(a) + np.abs(o0)) * 1.01 + 5e-5
+    err = np.abs(a - b)
+    G.report(f"v+1 causal={causal} {dtype}", max_err=float(err.max()))
+    assert np.all(err <= tol), f"out(v+1) - out(v) - 1: max {err.max():.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_last_row_sees_every_key(dtype):
+    B, Hq, Hkv, S, D = 2, 4, 2, 555, 128
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, dtype, seed=304)
+    dq, dk, dv = G.dev(q), G.dev(k), G.dev(v)
+    oc, lc = api.fwd(dq, dk, dv, causal=True)
+    on, ln_ = api.fwd(dq, dk, dv, causal=False)
+    torch.cuda.synchronize()
+    a, b = G.host(oc[:, :, -1]), G.host(on[:, :, -1])
+    # the two runs may move a row's reference max at different tiles (the
+    # move is decided per wave), so allow a rounding of each output and of
+    # the weights (relative u each, on weights summing to 1 over |v|)
+    vmax = float(np.abs(v.f32).max())
+    tol = 2 * ROUND[dtype] * (np.abs(a) + np.abs(b) + vmax) + 1e-5
+    assert np.all(np.abs(a - b) <= tol)
+    assert np.abs(G.host(lc[:, :, -1]) - G.host(ln_[:, :, -1])).max() <= (2e-3 if dtype == "bf16" else 1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_single_key_returns_v(D, dtype):
+    B, Hq, Hkv = 2, 4, 2
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, 1, D, dtype, seed=305)
+    sc = 1.0 / math.sqrt(D)
+    for causal in (True, False):
+        out, lse = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=causal, scale=sc)
+        torch.cuda.synchronize()
+        ref = torch.from_numpy(v.f32).repeat_interleave(Hq // Hkv, dim=1)
+        assert torch.equal(out.float().cpu(), ref)
+        k64 = np.repeat(k.f32.astype(np.float64), Hq // Hkv, axis=1)
+        ref_l = sc * (q.f32.astype(np.float64) * k64).sum(-1)
+        bound = D * 2.0 ** -24 * sc * (np.abs(q.f32.astype(np.float64)) * np.abs(k64)).sum(-1) + 1e-5
+        assert np.all(np.abs(G.host(lse) - ref_l) <= bound)
+
+
+def test_row0_bitwise_bf16():
+    q, k, v = inputs.make_qkv(2, 4, 2, 300, 128, "bf16", seed=306)
+    out, _ = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=True)
+    torch.cuda.synchronize()
+    ref = torch.from_numpy(v.f32[:, :, 0, :]).repeat_interleave(2, dim=1)
+    assert torch.equal(out[:, :, 0, :].float().cpu(), ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_gqa_equals_repeated_mha(causal, dtype):
+    B, Hq, Hkv, S, D = 1, 8, 2, 333, 128
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, dtype, seed=307)
+    dq, dk, dv = G.dev(q), G.dev(k), G.dev(v)
+    og, lg = api.fwd(dq, dk, dv, causal=causal)
+    om, lm = api.fwd(dq, dk.repeat_interleave(Hq // Hkv, dim=1).contiguous(),
+                     dv.repeat_interleave(Hq // Hkv, dim=1).contiguous(), causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(og, om) and torch.equal(lg, lm)
