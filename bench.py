@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--no-blockmask", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the fused causal forward at the other configurations (C1, C2, C4, C5)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--section-settle-s", type=float, default=0.3,
                     help="untimed launches before each extra section (backward, window, fp8, decode, unfused)")
@@ -411,6 +413,42 @@ def main():
                "frac_fp8_peak": round(f8tf / PEAK_FP8_TFLOPS, 4), "peak_fp8_tflops": PEAK_FP8_TFLOPS}
         del q8, k8, v8, o8
 
+    # the fused causal forward at the other configurations (bf16: C2 the
+    # 7B-LLaMA-like single sequence, C4 long context, C5 grouped-query; C1 the
+    # small fp32 case, latency only); N(0,1) draws on the device
+    configs = None
+    if not args.no_configs:
+        configs = {}
+        for name in ("C1", "C2", "C4", "C5"):
+            cc = inputs.CONFIGS[name]
+            cB, cHq, cHkv, cS, cD = cc["B"], cc["Hq"], cc["Hkv"], cc["S"], cc["D"]
+            csc = 1.0 / math.sqrt(cD)
+            f32 = cc["dtype"] == "f32"
+            gc = torch.Generator(device=dev)
+            gc.manual_seed(cc["seed"])
+            cq, ck, cv = [torch.randn(cB, h_, cS, cD, device=dev, generator=gc).to(torch.float32 if f32 else torch.bfloat16)
+                          for h_ in (cHq, cHkv, cHkv)]
+            co = torch.empty_like(cq)
+            cl = torch.empty((cB, cHq, cS), device=dev, dtype=torch.float32)
+            entry = _lib.attn_fwd_f32 if f32 else _lib.attn_fwd_bf16
+
+            def fwd_c(entry=entry, cq=cq, ck=ck, cv=cv, co=co, cl=cl, dims=(cB, cHq, cHkv, cS, cD), csc=csc):
+                rc = entry(cq.data_ptr(), ck.data_ptr(), cv.data_ptr(), co.data_ptr(), cl.data_ptr(), *dims, csc, 1, sp)
+                if rc:
+                    raise _lib.AttnError(rc, "attn_fwd")
+
+            fwd_c()
+            torch.cuda.synchronize()
+            settle_clock(fwd_c, args.section_settle_s)
+            cms = float(np.median(time_launches(fwd_c, 20, stream)))
+            ctf = attn_flops(cB, cHq, cS, cD, True) / (cms * 1e-3) / 1e12
+            configs[name] = {"workload": f"causal B{cB} Hq{cHq} Hkv{cHkv} S{cS} D{cD} {cc['dtype']}",
+                             "us": round(cms * 1e3, 2), "tflops": round(ctf, 2)}
+            if not f32:
+                configs[name]["frac_bf16_peak"] = round(ctf / PEAK_BF16_TFLOPS, 4)
+            del cq, ck, cv, co, cl
+        configs["data"] = "torch.randn on the device (generator seeded with the configuration's seed)"
+
     # split-KV decode step: one query per head of the GQA workload shape against a
     # 32768-key cache (attn_fwd_splitkv_bf16); bound by the K/V read
     decode = None
@@ -477,6 +515,7 @@ def main():
         "blockmask": blockmask,
         "decode": decode,
         "fp8": fp8,
+        "configs": configs,
         "gpu": props.name,
         "cus": props.multi_processor_count,
         "timed_wall_s": round(wall, 4),
