@@ -240,8 +240,36 @@ def main():
         "kernel": "fwd_bf16_kernel<128, causal>",
         "launch_ms_mean": round(ms_launch, 4),
         "launch_ms_min": round(float(np.min(per)), 4),
+        "launch_ms_median": round(float(np.median(per)), 4),
+        "launch_ms_p90": round(float(np.percentile(per, 90)), 4),
         "algorithmic_bytes": int(2 * B * Hq * S * D * 2 + 2 * B * Hkv * S * D * 2 + B * Hq * S * 4),
     }
+
+    # cold cache: 512 MB written between launches evicts q, k, v from the L2s
+    # and the MALL; each launch is timed alone with events on its stream
+    flush = torch.empty(128 << 20, device=dev, dtype=torch.float32)
+    cold = []
+    for _ in range(10):
+        flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fused()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    cold_ms = float(np.median(cold))
+    # host cost of one call through the C ABI (argument checks and the
+    # launch), launches queued without waiting
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for _ in range(50):
+        fused()
+    host_us = (time.perf_counter() - h0) / 50 * 1e6
+    torch.cuda.synchronize()
+    timing = {"cold_cache_ms_median": round(cold_ms, 4),
+              "cold_cache_tflops": round(flops / (cold_ms * 1e-3) / 1e12, 2),
+              "host_us_per_call": round(host_us, 2)}
 
     # non-causal fused, context
     per_nc = time_launches(lambda: fused(False), 10, stream)
@@ -516,6 +544,7 @@ def main():
         "decode": decode,
         "fp8": fp8,
         "configs": configs,
+        "timing": timing,
         "gpu": props.name,
         "cus": props.multi_processor_count,
         "timed_wall_s": round(wall, 4),
