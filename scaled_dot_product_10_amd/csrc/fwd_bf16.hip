@@ -80,6 +80,9 @@ struct Params {
 
 // Workgroups one XCD holds at once: 32 CUs per XCD, one 8-wave workgroup per CU.
 constexpr int kSlotsPerXcd = 32;
+// Grids of at most this many 256-query workgroups (one per CU) take the
+// key-split form: their time is the longest workgroup's.
+constexpr int64_t kSplitMaxWorkgroups = 8 * kSlotsPerXcd;
 
 // LDS tile layout: BN rows x D bf16, 16-byte chunks.  Chunk c of row r sits
 // at chunk position r*CPR + (c ^ swizzle(r)).
@@ -87,7 +90,6 @@ template <int D>
 struct Tile {
     static constexpr int CPR = D / 8;                 // chunks per row
     static constexpr int BYTES = BN * D * 2;          // 16 KB (D=128) / 8 KB (D=64)
-    static constexpr int DMA_PER_WAVE = BYTES / 1024 / NW;
     // K: the 16 rows one operand read touches per 16-lane phase land on 16
     // different bank groups (rows of 128 bytes alternate bank halves).
     __device__ static int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
@@ -100,14 +102,15 @@ struct Tile {
 // wave w fills LDS chunk positions p = (w*PER + i)*64 + lane; position p holds
 // chunk c = (p % CPR) ^ swizzle(r) of tile row r = p / CPR, so the lane fetches
 // byte offset r*2D + 16c from the tile's first row.
-template <int D, bool IS_V>
+template <int D, bool IS_V, int NWV = NW>
 struct DmaPlan {
     using T = Tile<D>;
-    uint32_t off[T::DMA_PER_WAVE];
+    static constexpr int PER = T::BYTES / 1024 / NWV;  // 1 KB instructions per wave and tile
+    uint32_t off[PER];
     __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-        for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
-            const int p = (wave * T::DMA_PER_WAVE + i) * 64 + lane;
+        for (int i = 0; i < PER; ++i) {
+            const int p = (wave * PER + i) * 64 + lane;
             const int r = p / T::CPR;
             const int c = (p % T::CPR) ^ (IS_V ? T::vswz(r) : T::kswz(r));
             off[i] = (uint32_t)(r * D * 2 + c * 16);
@@ -117,14 +120,14 @@ struct DmaPlan {
     // the sequence repeat row S-1 (those keys are masked and their P is 0)
     __device__ __forceinline__ void issue(const uint16_t* base, int n0, int S, char* tile, int wave) const {
         const uint16_t* tb = base + (int64_t)n0 * D;
-        const uint32_t l0 = lds_addr(tile) + (uint32_t)(wave * T::DMA_PER_WAVE) * 1024u;
+        const uint32_t l0 = lds_addr(tile) + (uint32_t)(wave * PER) * 1024u;
         if (n0 + BN <= S) {
 #pragma unroll
-            for (int i = 0; i < T::DMA_PER_WAVE; ++i) dma16(tb, off[i], l0 + i * 1024);
+            for (int i = 0; i < PER; ++i) dma16(tb, off[i], l0 + i * 1024);
         } else {
             const int last = S - 1 - n0;  // last valid row of this tile
 #pragma unroll
-            for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+            for (int i = 0; i < PER; ++i) {
                 const int r = (int)(off[i] / (D * 2));
                 const uint32_t o = off[i] - (uint32_t)((r - min(r, last)) * D * 2);
                 dma16(tb, o, l0 + i * 1024);
@@ -141,21 +144,32 @@ struct DmaPlan {
 // BLOCK: the loop runs over positions 0 .. npos-1 of the workgroup's list of
 // key tiles (tile number and one flag per query block); buffers alternate by
 // position.  Otherwise position n is tile n.
-template <int D, bool CAUSAL, bool LOCAL, bool BLOCK>
+// SPLIT (grids too small to fill the chip with 256-query workgroups): a
+// workgroup takes 128 queries; waves w and w+4 take the same 32 queries,
+// waves 0-3 the first half of the key tiles and waves 4-7 the second half,
+// each group with its own K/V buffers, in the same phase schedule.  At the
+// end waves 4-7 hand their (m, l, O) to their partners through LDS, which
+// merge them (the split-KV combination: both scaled to the larger m).  The
+// longest workgroup then runs half as many tiles.
+template <int D, bool CAUSAL, bool LOCAL, bool BLOCK, bool SPLIT>
 __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     static_assert(!LOCAL || CAUSAL, "a sliding window is a causal mask");
     static_assert(!(LOCAL && BLOCK), "one mask kind at a time");
+    static_assert(!SPLIT || (!LOCAL && !BLOCK), "the key split is for plain (causal or full) attention");
+    constexpr int BMK = SPLIT ? BM / 2 : BM;  // queries per workgroup
     using T = Tile<D>;
     constexpr int KS = D / 16;  // k-steps of the Q.K^T product
     constexpr int DB = D / 32;  // 32-row blocks of O^T
     constexpr int ROWB = T::CPR * 16;  // bytes per tile row
-    __shared__ __attribute__((aligned(1024))) char smem[4 * T::BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[(SPLIT ? 8 : 4) * T::BYTES];
     // BLOCK: listed key tiles (bits 0-23 tile, bit 24 + j: query block j may see it)
     __shared__ uint32_t blist[BLOCK ? kMaxMaskTiles + 2 : 1];
     __shared__ int bcount[BLOCK ? NW : 1];
-    // K buffers at [0, 2*BYTES), V buffers at [2*BYTES, 4*BYTES)
-    auto Kbuf = [&](int i) __attribute__((always_inline)) { return smem + (i & 1) * T::BYTES; };
-    auto Vbuf = [&](int i) __attribute__((always_inline)) { return smem + (2 + (i & 1)) * T::BYTES; };
+    // K buffers at [0, 2*BYTES), V buffers at [2*BYTES, 4*BYTES) (SPLIT: one
+    // such set per wave group)
+    const int gofs = SPLIT ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 8) * 4 * T::BYTES : 0;
+    auto Kbuf = [&](int i) __attribute__((always_inline)) { return smem + gofs + (i & 1) * T::BYTES; };
+    auto Vbuf = [&](int i) __attribute__((always_inline)) { return smem + gofs + (2 + (i & 1)) * T::BYTES; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     const int h = bh % p.Hq;
     const int kvh = h / p.group;
     const int S = p.S;
-    const int m0 = tile * BM;
+    const int m0 = tile * BMK;
 
     const int64_t row0 = (int64_t)bh * S;
     const uint16_t* qb = p.q + row0 * D;
@@ -199,13 +213,17 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     const uint16_t* kb = p.k + kvrow0 * D;
     const uint16_t* vb = p.v + kvrow0 * D;
 
-    const int qwmin = m0 + wave * 32;
+    const int qwmin = m0 + (SPLIT ? (wave & 3) : wave) * 32;
     const int qwmax = qwmin + 31;
     const int qi = qwmin + l32;
 
-    const int qlast = min(m0 + BM, S) - 1;
+    const int qlast = min(m0 + BMK, S) - 1;
     const int ntiles = (S + BN - 1) / BN;
-    int nend = CAUSAL ? min(ntiles, qlast / BN + 1) : ntiles;
+    const int nall = CAUSAL ? min(ntiles, qlast / BN + 1) : ntiles;  // key tiles of the workgroup
+    // SPLIT: each group runs nend positions; group 1's position n is tile
+    // toff + n, which may lie past the last tile (an idle position)
+    int nend = SPLIT ? (nall + 1) / 2 : nall;
+    const int toff = SPLIT && grp ? nend : 0;
     const int nbeg = LOCAL ? max(0, m0 - p.window + 1) / BN : 0;
 
     if (BLOCK) {
@@ -257,21 +275,26 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     // once per loop iteration; the key tile it names, and whether this wave's
     // query block may see that tile.
     auto ent = [&](int n) __attribute__((always_inline)) {
-        return BLOCK ? __builtin_amdgcn_readfirstlane(blist[n]) : (uint32_t)n;
+        return BLOCK ? __builtin_amdgcn_readfirstlane(blist[n]) : (uint32_t)(n + toff);
     };
     auto tile_of = [&](uint32_t e) __attribute__((always_inline)) { return BLOCK ? (int)(e & 0xffffffu) : (int)e; };
+    // SPLIT: the position names a tile of the workgroup
+    auto valid = [&](uint32_t e) __attribute__((always_inline)) { return !SPLIT || (int)e < nall; };
     auto wave_sees = [&](uint32_t e) __attribute__((always_inline)) {
         return !BLOCK || ((e >> (24 + wave / 2)) & 1u) != 0;
     };
 
     // ---- prologue: K(nbeg), V(nbeg), K(nbeg+1) in flight while Q is loaded --
-    DmaPlan<D, false> kdma;
-    DmaPlan<D, true> vdma;
-    kdma.init(wave, lane);
-    vdma.init(wave, lane);
-    kdma.issue(kb, tile_of(ent(nbeg)) * BN, S, Kbuf(nbeg), wave);
-    vdma.issue(vb, tile_of(ent(nbeg)) * BN, S, Vbuf(nbeg), wave);
-    if (nbeg + 1 < nend) kdma.issue(kb, tile_of(ent(nbeg + 1)) * BN, S, Kbuf(nbeg + 1), wave);
+    const int dw = SPLIT ? (wave & 3) : wave;  // wave's share of its group's tile loads
+    DmaPlan<D, false, SPLIT ? NW / 2 : NW> kdma;
+    DmaPlan<D, true, SPLIT ? NW / 2 : NW> vdma;
+    kdma.init(dw, lane);
+    vdma.init(dw, lane);
+    if (valid(ent(nbeg))) {
+        kdma.issue(kb, tile_of(ent(nbeg)) * BN, S, Kbuf(nbeg), dw);
+        vdma.issue(vb, tile_of(ent(nbeg)) * BN, S, Vbuf(nbeg), dw);
+    }
+    if (nbeg + 1 < nend && valid(ent(nbeg + 1))) kdma.issue(kb, tile_of(ent(nbeg + 1)) * BN, S, Kbuf(nbeg + 1), dw);
 
     // Q operand (B of S^T = K.Q^T): query qi, d = 16*ks + 8*g .. +7.
     bf16x8 qreg[KS];
@@ -426,7 +449,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     };
     auto softmax = [&](int n0) __attribute__((always_inline)) { softmax_impl(n0, std::true_type{}); };
 
-    auto active = [&](uint32_t e) __attribute__((always_inline)) { return !CAUSAL || tile_of(e) * BN <= qwmax; };
+    auto active = [&](uint32_t e) __attribute__((always_inline)) {
+        return valid(e) && (!CAUSAL || tile_of(e) * BN <= qwmax);
+    };
     // LOCAL: the tile holds a key this wave's first query sees (tiles before
     // every query's window are skipped, like tiles past the diagonal)
     auto in_window = [&](uint32_t e) __attribute__((always_inline)) {
@@ -493,8 +518,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     // DMA of K(k+1) and V(k) at the start of phase 2k (k >= 1); ek, ek1 the
     // entries of positions k, k+1
     auto dma_step = [&](int k, uint32_t ek, uint32_t ek1) __attribute__((always_inline)) {
-        if (k + 1 < nend) kdma.issue(kb, tile_of(ek1) * BN, S, Kbuf(k + 1), wave);
-        if (k < nend) vdma.issue(vb, tile_of(ek) * BN, S, Vbuf(k), wave);
+        if (k + 1 < nend && valid(ek1)) kdma.issue(kb, tile_of(ek1) * BN, S, Kbuf(k + 1), dw);
+        if (k < nend && valid(ek)) vdma.issue(vb, tile_of(ek) * BN, S, Vbuf(k), dw);
     };
 
     // Phase schedule (barrier after every phase; odd phases also wait for the
@@ -539,6 +564,33 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     // barrier) so that the stores cover whole rows: the wave's 32 rows are
     // contiguous in out, and each store instruction writes 1 KB (D = 128) of
     // them instead of 8 bytes per lane in 32 different rows.
+    if (SPLIT) {
+        // waves 4-7 hand (m, l, O) to their partners above group 0's output
+        // staging; the partners scale both halves to the larger m and add
+        constexpr int STG = (NW / 2) * 32 * D * 2;  // group 0's staging area
+        constexpr int WREG = DB * 16 * 64;          // floats of one wave's O
+        static_assert(STG + (NW / 2) * (WREG + 128) * 4 <= 8 * T::BYTES, "merge area fits");
+        float* mreg = (float*)(smem + STG) + (wave & 3) * (WREG + 128);
+        if (grp == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mreg[(db * 16 + r) * 64 + lane] = oacc[db][r];
+            mreg[WREG + lane] = mc;
+            mreg[WREG + 64 + lane] = lrow;
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        const float m1 = mreg[WREG + lane], l1 = mreg[WREG + 64 + lane];
+        const float mm = fmaxf(mc, m1);
+        const float a0 = fast_exp2(mc - mm), a1 = fast_exp2(m1 - mm);  // 0 for a half that saw no key
+        lrow = lrow * a0 + l1 * a1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + mreg[(db * 16 + r) * 64 + lane] * a1;
+        mc = mm;
+    }
     const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
     const float ltot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
     // BLOCK: a query block that sees no listed tile has l = 0: out 0, lse -inf
@@ -549,12 +601,12 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     if (qi < S && p.lse && g == 0) p.lse[row0 + qi] = seen ? (mc + __log2f(ltot)) * kLn2 : -INFINITY;
 }
 
-template <int D, bool CAUSAL, bool LOCAL = false, bool BLOCK = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BLOCK = false, bool SPLIT = false>
 hipError_t launch(const Params& prm, hipStream_t stream) {
     Params arg = prm;
     void* args[] = {&arg};
-    return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, CAUSAL, LOCAL, BLOCK>, dim3(prm.total), dim3(NT), args,
-                           0, stream);
+    return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, CAUSAL, LOCAL, BLOCK, SPLIT>, dim3(prm.total), dim3(NT),
+                           args, 0, stream);
 }
 
 }  // namespace
@@ -570,7 +622,13 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     prm.Hkv = a.Hkv;
     prm.S = a.S;
     prm.group = a.Hq / a.Hkv;
-    prm.nq = (a.S + BM - 1) / BM;
+    // plain attention whose 256-query grid would not fill the chip twice:
+    // 128-query workgroups with the key range split between the wave groups
+    const bool windowed = a.causal && a.window > 0 && a.window < a.S;
+    const bool split = !a.bmask && !windowed && a.S > BM &&
+                       (int64_t)a.B * a.Hq * ((a.S + BM - 1) / BM) <= kSplitMaxWorkgroups;
+    const int bmk = split ? BM / 2 : BM;
+    prm.nq = (a.S + bmk - 1) / bmk;
     prm.total = (uint32_t)((int64_t)a.B * a.Hq * prm.nq);
     prm.c = a.scale * kLog2e;
     prm.window = a.window;
@@ -594,6 +652,12 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     // a window of at least S keys hides nothing the causal mask shows
     if (a.causal && a.window > 0 && a.window < a.S)
         return a.D == 128 ? launch<128, true, true>(prm, stream) : launch<64, true, true>(prm, stream);
+    if (split) {
+        if (a.D == 128)
+            return a.causal ? launch<128, true, false, false, true>(prm, stream)
+                            : launch<128, false, false, false, true>(prm, stream);
+        return a.causal ? launch<64, true, false, false, true>(prm, stream) : launch<64, false, false, false, true>(prm, stream);
+    }
     if (a.D == 128) return a.causal ? launch<128, true>(prm, stream) : launch<128, false>(prm, stream);
     return a.causal ? launch<64, true>(prm, stream) : launch<64, false>(prm, stream);
 }

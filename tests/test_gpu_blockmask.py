@@ -80,7 +80,11 @@ def test_small_full_compare(orc, shape, density, causal):
 
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
 def test_all_ones_is_unmasked(causal):
-    q, k, v = inputs.make_qkv(2, 4, 2, 700, 128, "bf16", seed=7200)
+    # 288 workgroups of 256 queries: the plain kernel runs the same schedule
+    # as the block-mask one (smaller grids split each workgroup's key range
+    # between its two wave groups, which sums in another order), so the two
+    # agree bit for bit
+    q, k, v = inputs.make_qkv(2, 48, 2, 700, 128, "bf16", seed=7200)
     Q, K, V = G.dev(q), G.dev(k), G.dev(v)
     o1, l1 = api.fwd(Q, K, V, causal=causal)
     ones = torch.ones((1, 1, nblk(700), nblk(700)), dtype=torch.bool, device="cuda")
