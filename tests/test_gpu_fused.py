@@ -104,6 +104,23 @@ def test_long_sequence(orc, causal):
                   G.host(lse.view(-1)[idx]), ref_l)
 
 
+# Grids of more than 256 workgroups of 256 queries run the 256-query kernel
+# (the one the benchmark times); the small shapes above have fewer and take
+# the key-split form.  Full comparison of the former at ragged sizes, GQA.
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("shape", [(2, 72, 8, 300, 128), (1, 136, 17, 513, 64)],
+                         ids=lambda s: "B{}H{}kv{}S{}D{}".format(*s))
+def test_full_compare_256_query_schedule(orc, shape, causal):
+    B, Hq, Hkv, S, D = shape
+    assert B * Hq * ((S + 255) // 256) > 256
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", seed=401)
+    sc = 1.0 / math.sqrt(D)
+    out, lse = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    ref_o, ref_l = orc.attn_fwd(q.f32, k.f32, v.f32, sc, causal)
+    G.check_close(f"256-query {shape} causal={causal}", G.host(out), ref_o, "bf16", G.host(lse), ref_l)
+
+
 def test_row0_bitwise_f32():
     q, k, v = inputs.make_qkv(2, 4, 2, 70, 64, "f32", seed=77)
     out, _ = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=True)

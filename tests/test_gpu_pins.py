@@ -41,7 +41,9 @@ def _need_gpu():
 
 
 ROUND = {"bf16": 2.0 ** -8, "f32": 2.0 ** -24}  # unit roundoff of the output type
-SHAPES = [(1, 4, 2, 300, 128), (2, 2, 1, 129, 64)]  # ragged over 256-query and 64-key tiles
+# ragged over 256-query and 64-key tiles; the last shape has more than 256
+# workgroups of 256 queries (the 256-query kernel), the others fewer (key split)
+SHAPES = [(1, 4, 2, 300, 128), (2, 2, 1, 129, 64), (2, 72, 8, 300, 128)]
 
 
 def _prefix_mean(v64, causal):
