@@ -622,11 +622,15 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     prm.Hkv = a.Hkv;
     prm.S = a.S;
     prm.group = a.Hq / a.Hkv;
-    // plain attention whose 256-query grid would not fill the chip twice:
-    // 128-query workgroups with the key range split between the wave groups
+    // plain attention with at most one 256-query workgroup per CU: 128-query
+    // workgroups with the key range split between the wave groups.  Causal:
+    // the longest tile sets the time, and the split halves it.  Without the
+    // mask every workgroup is as long, and the split pays only while the
+    // doubled grid still runs in one round.
     const bool windowed = a.causal && a.window > 0 && a.window < a.S;
+    const int64_t g256 = (int64_t)a.B * a.Hq * ((a.S + BM - 1) / BM);
     const bool split = !a.bmask && !windowed && a.S > BM &&
-                       (int64_t)a.B * a.Hq * ((a.S + BM - 1) / BM) <= kSplitMaxWorkgroups;
+                       g256 <= (a.causal ? kSplitMaxWorkgroups : kSplitMaxWorkgroups / 2);
     const int bmk = split ? BM / 2 : BM;
     prm.nq = (a.S + bmk - 1) / bmk;
     prm.total = (uint32_t)((int64_t)a.B * a.Hq * prm.nq);
