@@ -107,34 +107,66 @@ def settle_clock(fn, seconds):
         torch.cuda.synchronize()
 
 
-def cpu_baseline(q, k, v, B, Hq, S, D, sc, seconds=12.0, seed=123):
+def cpu_baseline(q, k, v, B, Hq, S, D, sc, seconds=12.0, seed=123, causal=True, label=None):
     """The fp64 CPU oracle on random rows of the same workload until ~seconds
-    of wall time; rate in TFLOP/s with the same causal FLOP convention."""
+    of wall time (every row when the workload is smaller than that); rate in
+    TFLOP/s with the same FLOP convention (q.k and p.v over the visible keys)."""
     import oracle
 
     orc = oracle.default()
     threads = host_threads()
     rng = np.random.default_rng(seed)
+    n_rows = B * Hq * S
     done_rows, flops, t_total = 0, 0.0, 0.0
     chunk = 2048
-    while t_total < seconds:
-        rows = rng.integers(0, B * Hq * S, chunk)
+    while t_total < seconds and done_rows < n_rows:
+        if n_rows <= chunk:
+            rows = np.arange(n_rows, dtype=np.int64)
+        else:
+            rows = rng.integers(0, n_rows, chunk)
         i = rows % S
         t0 = time.perf_counter()
-        orc.attn_fwd(q.f32, k.f32, v.f32, sc, True, rows=rows, nthreads=threads)
+        orc.attn_fwd(q.f32, k.f32, v.f32, sc, causal, rows=rows, nthreads=threads)
         t_total += time.perf_counter() - t0
-        flops += float(np.sum(4.0 * (i + 1) * D))  # q.k and p.v over the i+1 visible keys
-        done_rows += chunk
+        keys = (i + 1) if causal else np.full(rows.size, S)
+        flops += float(np.sum(4.0 * keys * D))
+        done_rows += rows.size
         if t_total < 1.0:
             chunk *= 2
+    what = "every query row" if done_rows >= n_rows and n_rows <= chunk else f"{done_rows} random query rows"
     return {
         "value": flops / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done_rows} random query rows of the B4 H16 S4096 D128 causal workload "
-                  f"({flops / 1e9:.1f} GFLOP, {t_total:.1f} s, fp64, {cpu_model()})",
+        "sample": f"{what} of the {label or 'B4 H16 S4096 D128 causal'} workload "
+                  f"({flops / 1e9:.2f} GFLOP, {t_total:.2f} s, fp64, {cpu_model()})",
     }
+
+
+def stamped_clock(lib, args_fn, nrec, plain_fn, reps=5):
+    """Shader clock (GHz) of the fused bf16 kernel from its stamped launch:
+    per launch, the sum over workgroups of the clock-counter spans over the
+    sum of their 100 MHz real-time spans; the median over ``reps`` launches
+    that run back to back right after a few plain launches (the steady state
+    the timed loop sees).  Also the median launch span on the real-time
+    counter (first workgroup start to last end)."""
+    import torch
+
+    st = torch.zeros((reps, nrec, 8), dtype=torch.int64, device="cuda")
+    for _ in range(10):
+        plain_fn()
+    for r in range(reps):
+        rc = lib.attn_fwd_bf16_stamped(*args_fn(st[r].data_ptr()))
+        if rc:
+            raise lib.AttnError(rc, "attn_fwd_bf16_stamped")
+    torch.cuda.synchronize()
+    ghz, span = [], []
+    for rec in st.cpu().numpy():
+        rec = rec[rec[:, 1] != 0]
+        ghz.append(float((rec[:, 2] - rec[:, 0]).sum()) / float((rec[:, 3] - rec[:, 1]).sum()) * 0.1)
+        span.append(float(rec[:, 3].max() - rec[:, 1].min()) * 1e-5)  # ms
+    return float(np.median(ghz)), float(np.median(span))
 
 
 def main():
@@ -152,6 +184,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the fused causal forward at the other configurations (C1, C2, C4, C5)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds-config", type=float, default=2.0,
+                    help="oracle seconds for each of the other configurations")
     ap.add_argument("--section-settle-s", type=float, default=0.3,
                     help="untimed launches before each extra section (backward, window, fp8, decode, unfused)")
     ap.add_argument("--settle-s", type=float, default=0.5,
@@ -244,6 +278,17 @@ def main():
         "launch_ms_p90": round(float(np.percentile(per, 90)), 4),
         "algorithmic_bytes": int(2 * B * Hq * S * D * 2 + 2 * B * Hkv * S * D * 2 + B * Hq * S * 4),
     }
+
+    # the shader clock the kernel ran at (stamped launches of the same kernel)
+    # and the fraction of the matrix cores' peak at that clock
+    nrec = _lib.attn_fwd_bf16_stamp_bytes(B, Hq, S) // 64
+    sclk, span_ms = stamped_clock(
+        _lib, lambda stp: (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+                           S, D, sc, 1, stp, sp), nrec, fused)
+    roofline["sclk_ghz"] = round(sclk, 3)
+    roofline["peak_at_sclk"] = round(PEAK_BF16_TFLOPS * sclk / 2.4, 1)
+    roofline["frac_at_sclk"] = round(achieved / (PEAK_BF16_TFLOPS * sclk / 2.4), 4)
+    roofline["stamped_span_ms"] = round(span_ms, 4)
 
     # cold cache: 512 MB written between launches evicts q, k, v from the L2s
     # and the MALL; each launch is timed alone with events on its stream
@@ -443,7 +488,8 @@ def main():
 
     # the fused causal forward at the other configurations (bf16: C2 the
     # 7B-LLaMA-like single sequence, C4 long context, C5 grouped-query; C1 the
-    # small fp32 case, latency only); N(0,1) draws on the device
+    # small fp32 case, latency only), on the seeded inputs the parity tests
+    # use, with the oracle timed beside each on a bounded sample of its rows
     configs = None
     if not args.no_configs:
         configs = {}
@@ -452,15 +498,17 @@ def main():
             cB, cHq, cHkv, cS, cD = cc["B"], cc["Hq"], cc["Hkv"], cc["S"], cc["D"]
             csc = 1.0 / math.sqrt(cD)
             f32 = cc["dtype"] == "f32"
-            gc = torch.Generator(device=dev)
-            gc.manual_seed(cc["seed"])
-            cq, ck, cv = [torch.randn(cB, h_, cS, cD, device=dev, generator=gc).to(torch.float32 if f32 else torch.bfloat16)
-                          for h_ in (cHq, cHkv, cHkv)]
+            hq_, hk_, hv_ = inputs.make_qkv(cB, cHq, cHkv, cS, cD, cc["dtype"], cc["seed"])
+            if f32:
+                cq, ck, cv = [torch.from_numpy(t.f32).to(dev) for t in (hq_, hk_, hv_)]
+            else:
+                cq, ck, cv = [to_dev(t) for t in (hq_, hk_, hv_)]
             co = torch.empty_like(cq)
             cl = torch.empty((cB, cHq, cS), device=dev, dtype=torch.float32)
             entry = _lib.attn_fwd_f32 if f32 else _lib.attn_fwd_bf16
+            dims = (cB, cHq, cHkv, cS, cD)
 
-            def fwd_c(entry=entry, cq=cq, ck=ck, cv=cv, co=co, cl=cl, dims=(cB, cHq, cHkv, cS, cD), csc=csc):
+            def fwd_c(entry=entry, cq=cq, ck=ck, cv=cv, co=co, cl=cl, dims=dims, csc=csc):
                 rc = entry(cq.data_ptr(), ck.data_ptr(), cv.data_ptr(), co.data_ptr(), cl.data_ptr(), *dims, csc, 1, sp)
                 if rc:
                     raise _lib.AttnError(rc, "attn_fwd")
@@ -470,12 +518,26 @@ def main():
             settle_clock(fwd_c, args.section_settle_s)
             cms = float(np.median(time_launches(fwd_c, 20, stream)))
             ctf = attn_flops(cB, cHq, cS, cD, True) / (cms * 1e-3) / 1e12
-            configs[name] = {"workload": f"causal B{cB} Hq{cHq} Hkv{cHkv} S{cS} D{cD} {cc['dtype']}",
-                             "us": round(cms * 1e3, 2), "tflops": round(ctf, 2)}
+            entry_ = {"workload": f"causal B{cB} Hq{cHq} Hkv{cHkv} S{cS} D{cD} {cc['dtype']}",
+                      "us": round(cms * 1e3, 2), "tflops": round(ctf, 2)}
             if not f32:
-                configs[name]["frac_bf16_peak"] = round(ctf / PEAK_BF16_TFLOPS, 4)
-            del cq, ck, cv, co, cl
-        configs["data"] = "torch.randn on the device (generator seeded with the configuration's seed)"
+                entry_["frac_bf16_peak"] = round(ctf / PEAK_BF16_TFLOPS, 4)
+                cn = _lib.attn_fwd_bf16_stamp_bytes(cB, cHq, cS) // 64
+                cg, _ = stamped_clock(
+                    _lib, lambda stp, cq=cq, ck=ck, cv=cv, co=co, cl=cl, dims=dims, csc=csc: (
+                        cq.data_ptr(), ck.data_ptr(), cv.data_ptr(), co.data_ptr(), cl.data_ptr(), *dims, csc, 1,
+                        stp, sp), cn, fwd_c)
+                entry_["sclk_ghz"] = round(cg, 3)
+                entry_["frac_at_sclk"] = round(ctf / (PEAK_BF16_TFLOPS * cg / 2.4), 4)
+            if not args.no_cpu_baseline:
+                ob = cpu_baseline(hq_, hk_, hv_, cB, cHq, cS, cD, csc, seconds=args.cpu_seconds_config,
+                                  seed=cc["seed"], label=entry_["workload"])
+                entry_["oracle"] = {"tflops": ob["value"], "cores": ob["cores"], "sample": ob["sample"],
+                                    "gpu_speedup": round(ctf / ob["value"], 1)}
+            configs[name] = entry_
+            del cq, ck, cv, co, cl, hq_, hk_, hv_
+        configs["data"] = ("numpy PCG64 seeded with the configuration's seed, q, k, v drawn in that order, "
+                           "rounded to bf16 (the parity tests' inputs)")
 
     # split-KV decode step: one query per head of the GQA workload shape against a
     # 32768-key cache (attn_fwd_splitkv_bf16); bound by the K/V read

@@ -99,6 +99,31 @@ attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* 
                          void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Stamped fused forward (bfloat16): a measurement aid.
+ *
+ * Runs exactly the kernel attn_fwd_bf16 runs, with the same arguments and
+ * results, and in addition each workgroup w writes ATTN_STAMP_WORDS 64-bit
+ * words at stamps[w * ATTN_STAMP_WORDS]: the shader-clock counter and the
+ * 100 MHz real-time counter when it starts, the same two when its first wave
+ * has stored its output, its HW_ID and XCC_ID hardware registers (compute
+ * unit and die it ran on), and the (batch * Hq + head) and query tile it
+ * computed.  The ratio of the clock-counter span to the real-time span is the
+ * shader clock the kernel ran at, so its throughput can be set against the
+ * matrix cores' peak at that clock as well as at the nominal 2.4 GHz (the
+ * pages report per-op utilisation beside latency: the ainews.cool per-op
+ * table).  stamps: device memory of attn_fwd_bf16_stamp_bytes(B, Hq, S)
+ * bytes, 8-byte aligned, not overlapping any other argument; records of
+ * workgroups the launch does not have are left as they were (a launch uses
+ * at most B * Hq * ceil(S / 128) workgroups).  One kernel launch.
+ * ------------------------------------------------------------------------- */
+#define ATTN_STAMP_WORDS 8
+attn_status attn_fwd_bf16_stamped(const void* q, const void* k, const void* v, void* out, float* lse,
+                                  int B, int Hq, int Hkv, int S, int D, float scale, int causal,
+                                  uint64_t* stamps, void* stream);
+/* Bytes of attn_fwd_bf16_stamped's stamp records, or 0 on a bad size. */
+size_t attn_fwd_bf16_stamp_bytes(int B, int Hq, int S);
+
+/* ---------------------------------------------------------------------------
  * Fused forward with fp8 operands (OCP E4M3, "e4m3fn").
  *
  * q [B,Hq,S,D], k and v [B,Hkv,S,D]: one byte per element, e4m3fn codes;
@@ -183,6 +208,7 @@ size_t attn_splitkv_workspace_bytes(int B, int Hq, int Sq, int D, int nsplit);
 /* A split count that gives about two workgroups per compute unit, or 0 on a
  * bad size. */
 int attn_splitkv_default_splits(int B, int Hq, int Hkv, int Sq, int Skv);
+
 
 /* ---------------------------------------------------------------------------
  * Unfused trio, mirroring the naive pipeline one step per kernel.

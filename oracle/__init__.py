@@ -134,7 +134,12 @@ class Oracle:
 
     @staticmethod
     def _threads(nthreads):
-        return int(nthreads) if nthreads else (os.cpu_count() or 1)
+        if nthreads:
+            return int(nthreads)
+        try:
+            return len(os.sched_getaffinity(0))  # the CPUs this process may run on
+        except AttributeError:
+            return os.cpu_count() or 1
 
     @staticmethod
     def _check(rc: int, name: str):

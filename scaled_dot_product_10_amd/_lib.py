@@ -33,6 +33,8 @@ _i64 = ctypes.c_int64
 SIGNATURES = {
     "attn_fwd_bf16": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "attn_fwd_f32": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
+    "attn_fwd_bf16_stamped": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
+    "attn_fwd_bf16_stamp_bytes": (ctypes.c_size_t, [_i, _i, _i]),
     "attn_fwd_fp8": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _f, _f, _f, _i, _p]),
     "attn_fwd_local_bf16": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "attn_fwd_blockmask_bf16": (_i, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i, _i, _i, _i, _i, _f, _i, _p]),
@@ -88,6 +90,14 @@ def _call(name: str, *args) -> int:
 
 def attn_fwd_bf16(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, stream) -> int:
     return _call("attn_fwd_bf16", q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, stream)
+
+
+def attn_fwd_bf16_stamped(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, stamps, stream) -> int:
+    return _call("attn_fwd_bf16_stamped", q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, stamps, stream)
+
+
+def attn_fwd_bf16_stamp_bytes(B, Hq, S) -> int:
+    return int(lib().attn_fwd_bf16_stamp_bytes(B, Hq, S))
 
 
 def attn_fwd_f32(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, stream) -> int:

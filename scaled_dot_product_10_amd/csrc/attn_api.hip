@@ -178,6 +178,32 @@ attn_status attn_fwd_bf16(const void* q, const void* k, const void* v, void* out
                                             (hipStream_t)stream));
 }
 
+attn_status attn_fwd_bf16_stamped(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                                  int Hq, int Hkv, int S, int D, float scale, int causal, uint64_t* stamps,
+                                  void* stream) {
+    const attn_status st = check_fwd(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal, 2);
+    if (st != ATTN_OK) return st;
+    if (!stamps) return ATTN_ERR_NULL_POINTER;
+    if (misaligned(stamps, 8)) return ATTN_ERR_MISALIGNED;
+    const int64_t ns = prod({attn::fwd_bf16_max_workgroups(B, Hq, S), attn::kStampWords, 8});
+    if (ns < 0) return ATTN_ERR_BAD_SHAPE;
+    const int64_t nq = prod({B, Hq, S, D, 2});
+    const int64_t nkv = prod({B, Hkv, S, D, 2});
+    const int64_t nl = prod({B, Hq, S, 4});
+    if (overlap(stamps, ns, q, nq) || overlap(stamps, ns, k, nkv) || overlap(stamps, ns, v, nkv) ||
+        overlap(stamps, ns, out, nq) || overlap(stamps, ns, lse, nl))
+        return ATTN_ERR_ALIAS;
+    attn::FwdArgs a = fwd_args(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, causal);
+    a.stamps = (unsigned long long*)stamps;
+    return hip_status(attn::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+size_t attn_fwd_bf16_stamp_bytes(int B, int Hq, int S) {
+    if (B < 1 || Hq < 1 || S < 1) return 0;
+    const int64_t n = prod({attn::fwd_bf16_max_workgroups(B, Hq, S), attn::kStampWords, 8});
+    return n < 0 ? 0 : (size_t)n;
+}
+
 attn_status attn_fwd_local_bf16(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
                                 int Hkv, int S, int D, float scale, int window, void* stream) {
     const attn_status st = check_fwd(q, k, v, out, lse, B, Hq, Hkv, S, D, scale, 1, 2);
@@ -342,14 +368,16 @@ attn_status attn_pv_gemm_f32(const float* p, const float* v, float* out, int B, 
 
 constexpr int kMaxSplits = 4096;
 
-int64_t splitkv_ws_floats(int B, int Hq, int Sq, int D, int nsplit) {
+static int64_t splitkv_ws_floats(int B, int Hq, int Sq, int D, int nsplit) {
     return prod({nsplit, B, Hq, Sq, D + 1});
 }
 
-attn_status attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
-                                  float* workspace, int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
-                                  int causal, int nsplit, void* stream) {
-    if (!q || !k || !v || !out || !workspace) return ATTN_ERR_NULL_POINTER;
+// Checks shared by the two split-KV entry points; workspace may be null
+// (the allocation-free one) and is then not checked for alignment or overlap.
+static attn_status check_splitkv(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                          const float* workspace, int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                          int causal, int nsplit) {
+    if (!q || !k || !v || !out) return ATTN_ERR_NULL_POINTER;
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < Sq || Hq % Hkv != 0) return ATTN_ERR_BAD_SHAPE;
     if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
     if (causal != 0 && causal != 1) return ATTN_ERR_UNSUPPORTED;
@@ -372,6 +400,11 @@ attn_status attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, v
         overlap(workspace, nwb, q, nq) || overlap(workspace, nwb, k, nkv) || overlap(workspace, nwb, v, nkv) ||
         overlap(workspace, nwb, out, nq) || overlap(workspace, nwb, lse, nl))
         return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+static attn::SplitKvArgs splitkv_args(const void* q, const void* k, const void* v, void* out, float* lse, float* workspace,
+                               int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal, int nsplit) {
     attn::SplitKvArgs a;
     a.q = q;
     a.k = k;
@@ -388,7 +421,19 @@ attn_status attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, v
     a.scale = scale;
     a.causal = causal;
     a.nsplit = nsplit;
-    return hip_status(attn::launch_splitkv_bf16(a, (hipStream_t)stream));
+    return a;
+}
+
+attn_status attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
+                                  float* workspace, int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                                  int causal, int nsplit, void* stream) {
+    if (!workspace) return ATTN_ERR_NULL_POINTER;
+    const attn_status st =
+        check_splitkv(q, k, v, out, lse, workspace, B, Hq, Hkv, Sq, Skv, D, scale, causal, nsplit);
+    if (st != ATTN_OK) return st;
+    return hip_status(attn::launch_splitkv_bf16(
+        splitkv_args(q, k, v, out, lse, workspace, B, Hq, Hkv, Sq, Skv, D, scale, causal, nsplit),
+        (hipStream_t)stream));
 }
 
 size_t attn_splitkv_workspace_bytes(int B, int Hq, int Sq, int D, int nsplit) {

@@ -28,8 +28,9 @@
 //   and P^T is directly the B operand of the second product.  V^T comes from
 //   the row-major V tile through ds_read_b64_tr_b16, which hands each lane 4
 //   keys of one d, in the key order of the S^T accumulator rows.
-//   m is only moved when a row max exceeds it by more than 2^8 in p units
-//   (p stays <= 256, far from float32 overflow), so rescaling O is rare.
+//   The reference max m only moves when some lane's sum of p over a tile
+//   exceeds 2^12 (so every p stays <= 2^12, far from float32 overflow), so
+//   rescaling O is rare.
 //   Memory pipeline: K and V tiles go HBM -> LDS with global_load_lds_dwordx4
 //   (no register staging), double-buffered, each in flight for two phases.
 //   LDS rows are XOR-swizzled in 16-byte chunks so every operand read is free
@@ -76,6 +77,33 @@ struct Params {
     const uint8_t* bmask;
     int64_t bm_sb, bm_sh;
     int nkb;
+    // optional: kStampWords words per workgroup (see WgStamp)
+    uint64_t* stamps;
+};
+
+// Per-workgroup record of a stamped launch, written by lane 0 of wave 0:
+// shader-clock counter and 100 MHz real-time counter when the workgroup
+// starts and when that wave has stored its output, the hardware placement
+// registers, and the (batch * head, query tile) it ran.
+struct WgStamp {
+    uint64_t t0, r0;
+    __device__ __forceinline__ void start() {
+        t0 = __builtin_amdgcn_s_memtime();
+        r0 = __builtin_amdgcn_s_memrealtime();
+    }
+    __device__ __forceinline__ void finish(uint64_t* all, int bh, int tile) const {
+        const uint64_t t1 = __builtin_amdgcn_s_memtime();
+        const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+        uint64_t* s = all + (uint64_t)blockIdx.x * kStampWords;
+        s[0] = t0;
+        s[1] = r0;
+        s[2] = t1;
+        s[3] = r1;
+        s[4] = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID: wave, SIMD, CU, shader array, engine
+        s[5] = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID: which of the 8 dies
+        s[6] = (uint64_t)bh;
+        s[7] = (uint64_t)tile;
+    }
 };
 
 // Workgroups one XCD holds at once: 32 CUs per XCD, one 8-wave workgroup per CU.
@@ -172,6 +200,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     auto Vbuf = [&](int i) __attribute__((always_inline)) { return smem + gofs + (2 + (i & 1)) * T::BYTES; };
 
     const int tid = threadIdx.x;
+    const bool stamping = p.stamps != nullptr && tid == 0;
+    WgStamp stamp;
+    if (stamping) stamp.start();
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2;  // 0: waves 0-3 (one phase ahead), 1: waves 4-7
@@ -268,6 +299,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
                     for (int j = 0; j < 4; ++j) *(u32x2*)(orow + db * 32 + j * 8 + g * 4) = u32x2{0u, 0u};
                 if (p.lse && g == 0) p.lse[row0 + qi] = -INFINITY;
             }
+            if (stamping) stamp.finish(p.stamps, bh, tile);
             return;
         }
     }
@@ -411,8 +443,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
 
     // Softmax of tile n0 against the running reference max m.  Fast path: the
     // exponentials with the current m.  The reference only has to keep p
-    // bounded: when some lane's tile sum exceeds 2^12 (or is inf/NaN, as on the
-    // first tile, where m = -inf) the slow path takes the tile's row max
+    // bounded: when some lane's tile sum exceeds 2^12 (or is inf, as on the
+    // first tile, where m starts at -1e30 and every visible p overflows) the
+    // slow path takes the tile's row max
     // (exchanged between the two half-waves that share each query, so they keep
     // one reference), moves m, rescales O and l by 2^((m_old - m_new) c) and
     // redoes the exponentials, after which every p <= 1.
@@ -599,6 +632,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     static_assert(NW * 32 * D * 2 <= 4 * T::BYTES, "staging fits the K/V buffers");
     store_rows_via_lds<D>(smem + wave * 32 * D * 2, oacc, inv, p.out + (row0 + qwmin) * D, S - qwmin, lane);
     if (qi < S && p.lse && g == 0) p.lse[row0 + qi] = seen ? (mc + __log2f(ltot)) * kLn2 : -INFINITY;
+    if (stamping) stamp.finish(p.stamps, bh, tile);
 }
 
 template <int D, bool CAUSAL, bool LOCAL = false, bool BLOCK = false, bool SPLIT = false>
@@ -610,6 +644,11 @@ hipError_t launch(const Params& prm, hipStream_t stream) {
 }
 
 }  // namespace
+
+int64_t fwd_bf16_max_workgroups(int B, int Hq, int S) {
+    // the key-split form takes BM / 2 queries per workgroup, the others BM
+    return (int64_t)B * Hq * ((S + BM / 2 - 1) / (BM / 2));
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     Params prm;
@@ -640,6 +679,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     prm.bm_sb = a.bmask_stride_b;
     prm.bm_sh = a.bmask_stride_h;
     prm.nkb = (a.S + kMaskBlock - 1) / kMaskBlock;
+    prm.stamps = (uint64_t*)a.stamps;
     prm.hgrp = 0;
     const uint32_t per = prm.total / 8u;
     if (per > 0 && per % (uint32_t)prm.nq == 0) {

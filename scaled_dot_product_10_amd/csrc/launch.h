@@ -21,7 +21,13 @@ struct FwdArgs {
     // bmask[b * bmask_stride_b + h * bmask_stride_h + qb * ceil(S/64) + kb]; null: none
     const uint8_t* bmask = nullptr;
     int64_t bmask_stride_b = 0, bmask_stride_h = 0;
+    // bf16 only, optional: kStampWords 64-bit words per workgroup (stamped launch)
+    unsigned long long* stamps = nullptr;
 };
+
+constexpr int kStampWords = 8;
+// Workgroups a bf16 forward launch may use (stamp records to provide).
+int64_t fwd_bf16_max_workgroups(int B, int Hq, int S);
 
 struct QkArgs {
     const void* q;

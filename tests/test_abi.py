@@ -40,7 +40,7 @@ def L():
 
 def test_header_symbols_are_exported(L):
     syms = header_symbols()
-    assert len(syms) == 20, syms
+    assert len(syms) == 22, syms
     nm = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)], capture_output=True, text=True,
                         check=True).stdout
     exported = set(re.findall(r"\bT (\w+)$", nm, flags=re.M))
@@ -101,6 +101,24 @@ def fwd_args(**kw):
 ])
 def test_fwd_rejects(fn, kw, code):
     assert fn(*fwd_args(**kw)) == code
+
+
+def test_stamped_rejects():
+    f = _lib.attn_fwd_bf16_stamped
+    ST = A + (10 << 36)
+    # the forward's own checks come first
+    assert f(*fwd_args(q=None)[:-1], ST, None) == NULL
+    assert f(*fwd_args(D=96)[:-1], ST, None) == UNSUP
+    assert f(*fwd_args(out=A)[:-1], ST, None) == ALIAS
+    assert f(*fwd_args()[:-1], None, None) == NULL
+    assert f(*fwd_args()[:-1], ST + 4, None) == ALIGN
+    assert f(*fwd_args()[:-1], A + 64, None) == ALIAS   # stamps over q
+    assert f(*fwd_args()[:-1], Dp, None) == ALIAS       # stamps over out
+    assert f(*fwd_args()[:-1], E - 8, None) == ALIAS    # stamps running into lse
+    # B * Hq * ceil(S / 128) records of 8 words
+    assert _lib.attn_fwd_bf16_stamp_bytes(4, 16, 4096) == 4 * 16 * 32 * 8 * 8
+    assert _lib.attn_fwd_bf16_stamp_bytes(1, 1, 1) == 64
+    assert _lib.attn_fwd_bf16_stamp_bytes(0, 1, 8) == 0
 
 
 def test_fp8_rejects():
@@ -258,3 +276,72 @@ def test_missing_library_is_loud(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_LIB", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         _lib.lib()
+
+
+# ---------------------------------------------------------------------------
+# The torch front end checks every tensor's dtype and exact shape before the
+# device (the C ABI cannot see buffer sizes, so an undersized out, lse or
+# score buffer would otherwise be written out of bounds).  CPU tensors reach
+# every shape check here; with correct shapes they stop at the GPU check.
+# ---------------------------------------------------------------------------
+torch = pytest.importorskip("torch")
+from scaled_dot_product_10_amd import api  # noqa: E402
+
+
+def _t(*shape, dtype=None):
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def _raises(match, fn, *a, exc=ValueError, **kw):
+    with pytest.raises(exc, match=match):
+        fn(*a, **kw)
+
+
+def test_api_fwd_checks_shapes():
+    q, k, v = _t(1, 4, 8, 64), _t(1, 2, 8, 64), _t(1, 2, 8, 64)
+    _raises("k must have shape", api.fwd, q, _t(1, 2, 9, 64), v)
+    _raises("v must have shape", api.fwd, q, k, _t(1, 2, 8, 32))
+    _raises("out must have shape", api.fwd, q, k, v, out=_t(1, 4, 7, 64))
+    _raises("lse must have shape", api.fwd, q, k, v, lse=_t(1, 4, 7, dtype=torch.float32))
+    _raises("lse must be", api.fwd, q, k, v, lse=_t(1, 4, 8), exc=TypeError)
+    _raises("out must be", api.fwd, q, k, v, out=_t(1, 4, 8, 64, dtype=torch.float32), exc=TypeError)
+    _raises("must be a GPU tensor", api.fwd, q, k, v)
+
+
+def test_api_unfused_checks_shapes():
+    q, k = _t(1, 2, 8, 64), _t(1, 1, 8, 64)
+    _raises("k must have shape", api.qk_gemm, q, _t(1, 1, 8, 128))
+    _raises("scores must have shape", api.qk_gemm, q, k, scores=_t(1, 2, 8, 7, dtype=torch.float32))
+    _raises("must be a GPU tensor", api.qk_gemm, q, k)
+    sc = _t(1, 2, 8, 8, dtype=torch.float32)
+    _raises("p must have shape", api.masked_softmax, sc, scale=0.1, p=_t(1, 2, 8, 4))
+    _raises("lse must have shape", api.masked_softmax, sc, scale=0.1, lse=_t(1, 2, 9, dtype=torch.float32))
+    _raises("must be a GPU tensor", api.masked_softmax, sc, scale=0.1)
+    p, v = _t(1, 2, 8, 8), _t(1, 1, 8, 64)
+    _raises("p must be", api.pv_gemm, _t(1, 2, 8, 9), v)
+    _raises("v must have shape", api.pv_gemm, p, _t(1, 1, 9, 64))
+    _raises("v must have shape", api.pv_gemm, p, _t(2, 1, 8, 64))
+    _raises("out must have shape", api.pv_gemm, p, v, out=_t(1, 2, 8, 32))
+    _raises("must be a GPU tensor", api.pv_gemm, p, v)
+
+
+def test_api_bwd_splitkv_fp8_check_shapes():
+    q, k, v = _t(1, 2, 8, 64), _t(1, 1, 8, 64), _t(1, 1, 8, 64)
+    lse = _t(1, 2, 8, dtype=torch.float32)
+    _raises("out must have shape", api.bwd, q, k, v, _t(1, 2, 8, 32), lse, q)
+    _raises("dout must have shape", api.bwd, q, k, v, q, lse, _t(1, 2, 4, 64))
+    _raises("lse must have shape", api.bwd, q, k, v, q, _t(1, 2, 9, dtype=torch.float32), q)
+    _raises("delta must have shape", api.bwd, q, k, v, q, lse, q, delta=_t(1, 1, 8, dtype=torch.float32))
+    _raises("must be a GPU tensor", api.bwd, q, k, v, q, lse, q)
+    qd, kd = _t(1, 2, 1, 64), _t(1, 1, 40, 64)
+    _raises("v must have shape", api.fwd_splitkv, qd, kd, _t(1, 1, 39, 64), nsplit=2)
+    _raises("out must have shape", api.fwd_splitkv, qd, kd, kd, nsplit=2, out=_t(1, 2, 2, 64))
+    _raises("lse must have shape", api.fwd_splitkv, qd, kd, kd, nsplit=2, lse=_t(1, 2, 2, dtype=torch.float32))
+    _raises("workspace must be", api.fwd_splitkv, qd, kd, kd, nsplit=2, workspace=_t(1, dtype=torch.float32))
+    _raises("must be a GPU tensor", api.fwd_splitkv, qd, kd, kd, nsplit=2)
+    u8 = torch.uint8
+    q8, k8 = _t(1, 2, 8, 64, dtype=u8), _t(1, 1, 8, 64, dtype=u8)
+    _raises("v must have shape", api.fwd_fp8, q8, k8, _t(1, 1, 8, 128, dtype=u8), 1.0, 1.0, 1.0)
+    _raises("out must have shape", api.fwd_fp8, q8, k8, k8, 1.0, 1.0, 1.0, out=_t(1, 2, 8, 32))
+    _raises("lse must have shape", api.fwd_fp8, q8, k8, k8, 1.0, 1.0, 1.0, lse=_t(2, 2, 8, dtype=torch.float32))
+    _raises("must be a GPU tensor", api.fwd_fp8, q8, k8, k8, 1.0, 1.0, 1.0)

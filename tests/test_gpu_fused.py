@@ -1,10 +1,10 @@
 """Fused forward (attn_fwd_bf16 / attn_fwd_f32) against the fp64 CPU oracle.
 
 Small shapes are compared element by element over the whole output; they span
-several 128-query and 64-key tiles and ragged tails.  The full workloads (the
-five measured configurations, in the launch configuration the bench times)
-are compared on sampled rows, which the oracle computes one at a time, plus
-properties checked over every row.
+several 128-query and 64-key tiles and ragged tails.  The five measured
+configurations are compared element by element too, over every row of out and
+lse, in the launch configuration the bench times.  Longer sequences are
+compared on sampled rows, which the oracle computes one at a time.
 """
 from __future__ import annotations
 
@@ -43,7 +43,7 @@ def test_small_full_compare(orc, shape, causal, dtype):
     out, lse = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=causal, scale=sc)
     torch.cuda.synchronize()
     ref_o, ref_l = orc.attn_fwd(q.f32, k.f32, v.f32, sc, causal)
-    G.check_close(f"fwd {dtype} {shape} causal={causal}", G.host(out), ref_o, dtype, G.host(lse), ref_l)
+    G.check_close(f"fwd {dtype} {shape} causal={causal}", G.host(out), ref_o, dtype, G.host(lse), ref_l, keys=S)
 
 
 # ---------------------------------------------------------------------------
@@ -64,28 +64,23 @@ def workload(name):
 @pytest.mark.parametrize("name,causal", [("C1", True), ("C2", True), ("C3", True), ("C3", False), ("C4", True),
                                          ("C5", True)])
 def test_config(orc, name, causal):
+    """Every element of out and lse of the configuration, in the launch the
+    benchmark times, against the oracle (the oracle runs on all host threads:
+    about 1 s for C2, 6 s for C3 causal, 25 s for C4 and C5)."""
     c, q, k, v, dq, dk, dv = workload(name)
     B, Hq, S, D = c["B"], c["Hq"], c["S"], c["D"]
     sc = 1.0 / math.sqrt(D)
     out, lse = api.fwd(dq, dk, dv, causal=causal, scale=sc)
     torch.cuda.synchronize()
-    if name == "C1":
-        ref_o, ref_l = orc.attn_fwd(q.f32, k.f32, v.f32, sc, causal)
-        G.check_close(f"{name} causal={causal}", G.host(out), ref_o, c["dtype"], G.host(lse), ref_l)
-        return
-    rows = G.sample_rows(B, Hq, S, n_random=400, seed=c["seed"])
-    ref_o, ref_l = orc.attn_fwd(q.f32, k.f32, v.f32, sc, causal, rows=rows)
-    o = out.view(-1, D)[torch.from_numpy(rows).to(out.device)]
-    l = lse.view(-1)[torch.from_numpy(rows).to(out.device)]
-    G.check_close(f"{name} causal={causal} rows={rows.size}", G.host(o), ref_o, c["dtype"], G.host(l), ref_l)
-    # every row written and finite
-    assert bool(torch.isfinite(lse).all())
-    assert bool(torch.isfinite(out.float()).all())
     if causal:
         # row 0 sees key 0 only: out = v_0 bit for bit (p = 1, l = 1)
         g = Hq // c["Hkv"]
         v0 = dv[:, :, 0, :].repeat_interleave(g, dim=1)
         assert torch.equal(out[:, :, 0, :], v0)
+    got_o, got_l = G.host(out), G.host(lse)
+    del out, lse
+    ref_o, ref_l = orc.attn_fwd(q.f32, k.f32, v.f32, sc, causal)
+    G.check_close(f"{name} causal={causal} all {B * Hq * S} rows", got_o, ref_o, c["dtype"], got_l, ref_l, keys=S)
 
 
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
@@ -118,7 +113,7 @@ def test_full_compare_256_query_schedule(orc, shape, causal):
     out, lse = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=causal, scale=sc)
     torch.cuda.synchronize()
     ref_o, ref_l = orc.attn_fwd(q.f32, k.f32, v.f32, sc, causal)
-    G.check_close(f"256-query {shape} causal={causal}", G.host(out), ref_o, "bf16", G.host(lse), ref_l)
+    G.check_close(f"256-query {shape} causal={causal}", G.host(out), ref_o, "bf16", G.host(lse), ref_l, keys=S)
 
 
 def test_row0_bitwise_f32():
@@ -189,5 +184,43 @@ def test_large_logits(orc, dtype):
     u = 2.0 ** -23
     absdot = np.matmul(np.abs(qs.f32.astype(np.float64)),
                        np.abs(np.repeat(k.f32, Hq // Hkv, axis=1).astype(np.float64)).transpose(0, 1, 3, 2))
-    lse_tol = D * u / (1 - D * u) * sc * float(absdot.max()) + G.LSE_TOL[dtype]
+    lse_tol = D * u / (1 - D * u) * sc * float(absdot.max()) + G.lse_bound(dtype, S)
     G.check_close(f"large logits {dtype}", G.host(out), ref_o, dtype, G.host(lse), ref_l, lse_tol=lse_tol)
+
+
+@pytest.mark.parametrize("name,causal", [("C3", True), ("C2", True), ("C3", False)])
+def test_stamped_launch(name, causal):
+    """The stamped launch runs the same kernel: bit-identical results; every
+    workgroup of the grid leaves one record, the records cover each
+    (head, query tile) once, and the counters advance."""
+    from scaled_dot_product_10_amd import _lib
+
+    c, q, k, v, dq, dk, dv = workload(name)
+    B, Hq, Hkv, S, D = c["B"], c["Hq"], c["Hkv"], c["S"], c["D"]
+    sc = 1.0 / math.sqrt(D)
+    out0, lse0 = api.fwd(dq, dk, dv, causal=causal, scale=sc)
+    out = torch.empty_like(out0)
+    lse = torch.empty_like(lse0)
+    nrec = _lib.attn_fwd_bf16_stamp_bytes(B, Hq, S) // 64
+    st = torch.zeros((nrec, 8), dtype=torch.int64, device=dq.device)
+    rc = _lib.attn_fwd_bf16_stamped(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                    B, Hq, Hkv, S, D, sc, int(causal), st.data_ptr(),
+                                    torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out, out0) and torch.equal(lse, lse0)
+    rec = st.cpu().numpy()
+    used = rec[:, 1] != 0
+    n = int(used.sum())
+    assert used[:n].all(), "records must be the first n slots (one per workgroup)"
+    rec = rec[:n]
+    qt = (S + n // (B * Hq) - 1) // (n // (B * Hq))  # queries per workgroup
+    assert n == B * Hq * ((S + qt - 1) // qt) and qt in (128, 256)
+    pairs = set(zip(rec[:, 6].tolist(), rec[:, 7].tolist()))
+    assert pairs == {(bh, t) for bh in range(B * Hq) for t in range(n // (B * Hq))}
+    dt = rec[:, 2] - rec[:, 0]
+    dr = rec[:, 3] - rec[:, 1]
+    assert (dt > 0).all() and (dr > 0).all()
+    ghz = dt.sum() / dr.sum() * 0.1  # real-time counter at 100 MHz
+    G.report(f"stamped {name} causal={causal}", workgroups=n, sclk_ghz=float(ghz))
+    assert 0.3 < ghz < 3.0

@@ -41,9 +41,13 @@ def _need_gpu():
 
 
 ROUND = {"bf16": 2.0 ** -8, "f32": 2.0 ** -24}  # unit roundoff of the output type
-# ragged over 256-query and 64-key tiles; the last shape has more than 256
-# workgroups of 256 queries (the 256-query kernel), the others fewer (key split)
-SHAPES = [(1, 4, 2, 300, 128), (2, 2, 1, 129, 64), (2, 72, 8, 300, 128)]
+# ragged over 256-query and 64-key tiles.  The key split (128-query
+# workgroups whose wave groups split the key range) runs when S > 256 and the
+# grid has at most 256 workgroups of 256 queries: the first and fourth shapes
+# (D = 128 and D = 64).  The second has S <= 256 (plain 256-query form on a
+# small grid); the third has more than 256 workgroups of 256 queries (the
+# 256-query kernel the benchmark times).
+SHAPES = [(1, 4, 2, 300, 128), (2, 2, 1, 129, 64), (2, 72, 8, 300, 128), (1, 2, 1, 300, 64)]
 
 
 def _prefix_mean(v64, causal):
