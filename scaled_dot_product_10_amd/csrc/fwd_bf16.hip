@@ -144,6 +144,22 @@ struct DmaPlan {
             off[i] = (uint32_t)(r * D * 2 + c * 16);
         }
     }
+    // Rows of a tile whose first row is at tb into LDS at byte address l0 (the
+    // whole tile's), this wave's share; with full = false, rows past row
+    // `last` of the tile repeat that row.
+    __device__ __forceinline__ void issue_at(const uint16_t* tb, bool full, int last, uint32_t l0, int wave) const {
+        const uint32_t lw = l0 + (uint32_t)(wave * PER) * 1024u;
+        if (full) {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) dma16(tb, off[i], lw + i * 1024);
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int r = (int)(off[i] / (D * 2));
+                dma16(tb, off[i] - (uint32_t)((r - min(r, last)) * D * 2), lw + i * 1024);
+            }
+        }
+    }
     // rows n0 .. n0+BN-1 of the head starting at base; rows past the end of
     // the sequence repeat row S-1 (those keys are masked and their P is 0)
     __device__ __forceinline__ void issue(const uint16_t* base, int n0, int S, char* tile, int wave) const {
@@ -635,6 +651,474 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     if (stamping) stamp.finish(p.stamps, bh, tile);
 }
 
+// ---------------------------------------------------------------------------
+// Persistent form (plain causal or full attention, S >= BM): one workgroup per
+// compute unit runs a fixed list of (head, query tile) items back to back.
+// The key/value tile stream and the two wave groups' phase schedule run on
+// across item boundaries, so an item's start costs no pipeline fill: while
+// the last tiles of one item are processed, the first key/value tiles of the
+// next are already in flight, and its Q rows wait in LDS (each wave brings in
+// its own 32 rows by LDS DMA during the previous item and copies them into
+// registers at that item's last softmax phase).  The previous item's output
+// is normalised and stored during the next item's first softmax phase.
+//
+// Items: each head's query tiles form units; causal: unit j = tiles nq-1-j
+// and j (a long and a short item with 4 (nq + 1) key tiles together, so every
+// unit is equally long); full: unit j = tile j.  Workgroup w runs unit
+// r G + (w % 8) G/8 + w / 8 in round r: workgroups on one XCD (the hardware
+// deals them round-robin over the 8 XCDs) take consecutive units, i.e. the
+// tiles of a few heads, whose key/value tiles they read in step through the
+// XCD's L2.
+struct PersistParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* out;
+    float* lse;
+    int Hq, Hkv, S, group, nq;
+    int units;   // units per head (causal nq / 2, full nq)
+    int rounds;  // units per workgroup
+    float c;     // scale * log2(e), > 0
+    uint64_t* stamps;
+};
+
+// A zero the compiler cannot see through.  Per-lane addresses used once per
+// item (Q DMA, output staging) are derived from lane | opaque_zero() inside
+// the loop, so they are computed where they are used instead of being
+// hoisted out of the loop and held in registers for the whole kernel.
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
+    using T = Tile<D>;
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int ROWB = T::CPR * 16;
+    constexpr int QWB = 32 * D * 2;  // bytes of one wave's 32 Q rows
+    constexpr int QPER = QWB / 1024; // its DMA instructions
+    __shared__ __attribute__((aligned(1024))) char smem[4 * T::BYTES + NW * QWB];
+    auto Kbuf = [&](int i) __attribute__((always_inline)) { return smem + (i & 1) * T::BYTES; };
+    auto Vbuf = [&](int i) __attribute__((always_inline)) { return smem + (2 + (i & 1)) * T::BYTES; };
+
+    const int tid = threadIdx.x;
+    const bool stamping = p.stamps != nullptr && tid == 0;
+    WgStamp stamp;
+    if (stamping) stamp.start();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    char* const qst = smem + 4 * T::BYTES + wave * QWB;  // this wave's Q rows (K-tile layout)
+    const int S = p.S;
+    const int ntiles = (S + BN - 1) / BN;
+    const int nitems = p.rounds * (CAUSAL ? 2 : 1);
+    const uint32_t G = gridDim.x;
+    // XCD x (blockIdx % 8) runs units [x U/8, (x+1) U/8) of all U = rounds G:
+    // consecutive heads, G/8 units per round
+    const uint32_t xbase = (blockIdx.x % 8u) * (uint32_t)p.rounds * (G / 8u) + blockIdx.x / 8u;
+
+    // item i of this workgroup -> (b * Hq + h, query tile); key tiles it runs
+    auto item_bh_tile = [&](int i, int& bh, int& tile) __attribute__((always_inline)) {
+        const int r = CAUSAL ? i >> 1 : i;
+        const uint32_t L = xbase + (uint32_t)r * (G / 8u);
+        bh = (int)(L / (uint32_t)p.units);
+        const int j = (int)(L % (uint32_t)p.units);
+        tile = CAUSAL ? ((i & 1) ? j : p.nq - 1 - j) : j;
+    };
+    auto item_tiles = [&](int tile) __attribute__((always_inline)) {
+        return CAUSAL ? min(ntiles, (min(tile * BM + BM, S) - 1) / BN + 1) : ntiles;
+    };
+    // The stream position: key tile k of the current item (nk key tiles,
+    // head bh, query tile); the next item's head and query tile.  Every item
+    // has at least 4 key tiles, so the two positions after the current one
+    // lie in these two items.
+    int it = 0, k = 0, nk, bh, tile;
+    int nbh = 0, ntile = 0;
+    auto kv_of = [&](int bh_) __attribute__((always_inline)) {
+        const int b = bh_ / p.Hq, h = bh_ % p.Hq;
+        return ((int64_t)b * p.Hkv + h / p.group) * S * D;  // element offset of the head's key 0
+    };
+    item_bh_tile(0, bh, tile);
+    nk = item_tiles(tile);
+    bool has_next = nitems > 1;
+    if (has_next) item_bh_tile(1, nbh, ntile);
+    // DMA sources: K of position n+2 and V of position n+1 (tile pointers
+    // that advance one tile per position and jump to the next item's first
+    // key at the crossing), and their key tiles within their items
+    constexpr int64_t TSTEP = (int64_t)BN * D;  // elements per key tile
+    const int64_t kv0 = kv_of(bh);
+    int64_t knext = has_next ? kv_of(nbh) : 0;  // next item's key 0
+    const uint16_t* kp = p.k + kv0 + 2 * TSTEP;
+    const uint16_t* vp = p.v + kv0 + TSTEP;
+    auto advance_item = [&]() __attribute__((always_inline)) {
+        ++it;
+        bh = nbh;
+        tile = ntile;
+        nk = item_tiles(tile);
+        k = 0;
+        has_next = it + 1 < nitems;
+        if (has_next) {
+            item_bh_tile(it + 1, nbh, ntile);
+            knext = kv_of(nbh);
+        }
+    };
+
+    DmaPlan<D, false> kdma;
+    DmaPlan<D, true> vdma;
+    kdma.init(wave, lane);
+    vdma.init(wave, lane);
+    // DMA of this wave's 32 Q rows (first row r0 of head bh_) into qst, laid
+    // out like a K tile (row r, chunk c at c ^ kswz(r)); rows past the end of
+    // the sequence repeat row S - 1 (their results are never stored)
+    auto q_dma = [&](int bh_, int tile_) __attribute__((always_inline)) {
+        const int ln = lane | opaque_zero();  // offsets computed here, not held across the loop
+        const int r0 = tile_ * BM + wave * 32;
+        const uint16_t* base = p.q + ((int64_t)bh_ * S + min(r0, S - 1)) * D;
+        const int last = S - 1 - min(r0, S - 1);  // last row of the 32 inside the sequence
+        const uint32_t l0 = lds_addr(qst);
+#pragma unroll
+        for (int i = 0; i < QPER; ++i) {
+            const int pos = i * 64 + ln;
+            const int r = pos / T::CPR;
+            const int cc = (pos % T::CPR) ^ T::kswz(r);
+            dma16(base, (uint32_t)(min(r, last) * D * 2 + cc * 16), l0 + i * 1024);
+        }
+    };
+
+    int koff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = l32 * ROWB + (((2 * ks + g) ^ T::kswz(l32)) * 16);
+    int voff[DB];
+    {
+        const int Gq = lane >> 4, j = lane & 15;
+        const int r = 4 * (Gq >> 1) + (j >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int d0 = db * 32 + (Gq & 1) * 16 + 4 * (j & 3);
+            voff[db] = r * ROWB + (((d0 >> 3) ^ T::vswz(r)) * 16) + (d0 & 7) * 2;
+        }
+    }
+    bf16x8 qreg[KS];
+    // Q rows from LDS into the operand registers (once per item).
+    auto q_read = [&]() __attribute__((always_inline)) {
+        const int z = opaque_zero();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qreg[ks] = *(const bf16x8*)(qst + (koff[ks] | z));
+    };
+
+    // ---- prologue: Q of the first item, K(0), V(0), K(1) ---------------------
+    q_dma(bh, tile);
+    kdma.issue(p.k + kv0, 0, S, Kbuf(0), wave);
+    vdma.issue(p.v + kv0, 0, S, Vbuf(0), wave);
+    kdma.issue(p.k + kv0, BN, S, Kbuf(1), wave);  // the item has 4 or more key tiles
+    phase_barrier(true);
+    q_read();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+    const float c = p.c;
+    // the item whose softmax and output this wave is on
+    int qwmin = tile * BM + wave * 32;
+    int qwmax = qwmin + 31;
+    int qi = qwmin + l32;
+    int64_t row0 = (int64_t)bh * S;
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    float mc = -1e30f;  // reference max (see fwd_bf16_kernel); finite, so no inf - inf
+    float lrow = 0.f;
+    f32x16 sacc[2];
+    bf16x8 pb[4];
+
+    auto qk = [&](const char* Kt) __attribute__((always_inline)) {
+        constexpr int NP = 2 * KS;
+        auto rd = [&](int i) __attribute__((always_inline)) { return *(const bf16x8*)(Kt + koff[i >> 1] + (i & 1) * 32 * ROWB); };
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
+        bf16x8 a0 = rd(0), a1 = rd(1);
+#pragma unroll
+        for (int i = 0; i < NP; i += 2) {
+            bf16x8 n0, n1;
+            if (i + 2 < NP) {
+                n0 = rd(i + 2);
+                n1 = rd(i + 3);
+            }
+            sacc[0] = mfma32x32x16(a0, qreg[i >> 1], sacc[0]);
+            sacc[1] = mfma32x32x16(a1, qreg[i >> 1], sacc[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            a0 = n0;
+            a1 = n1;
+        }
+    };
+    auto pv = [&](const char* Vt) __attribute__((always_inline)) {
+        auto rd = [&](int i) __attribute__((always_inline)) {
+            const char* base = Vt + voff[i % DB] + (i / DB) * 16 * ROWB;
+            return tr_read_pair(base, base + 8 * ROWB);
+        };
+        constexpr int NP = 4 * DB;
+        bf16x8 a0 = rd(0), a1 = rd(1);
+#pragma unroll
+        for (int i = 0; i < NP; i += 2) {
+            bf16x8 n0, n1;
+            if (i + 2 < NP) {
+                n0 = rd(i + 2);
+                n1 = rd(i + 3);
+            }
+            oacc[i % DB] = mfma32x32x16(a0, pb[i / DB], oacc[i % DB]);
+            oacc[(i + 1) % DB] = mfma32x32x16(a1, pb[(i + 1) / DB], oacc[(i + 1) % DB]);
+            __builtin_amdgcn_sched_barrier(0);
+            a0 = n0;
+            a1 = n1;
+        }
+    };
+    auto exp_pack = [&](float mref) __attribute__((always_inline)) {
+        float ps[4];
+#pragma unroll
+        for (int kb16 = 0; kb16 < 4; ++kb16) {
+            const int sb = kb16 >> 1, hh = kb16 & 1;
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = fast_exp2(fmaf(sacc[sb][hh * 8 + 2 * e], c, -mref));
+                const float p1 = fast_exp2(fmaf(sacc[sb][hh * 8 + 2 * e + 1], c, -mref));
+                w[e] = pack_bf16x2(p0, p1);
+                ps[e] = kb16 == 0 ? p0 + p1 : ps[e] + (p0 + p1);
+            }
+            pb[kb16] = as_bf16x8(w);
+        }
+        return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+    // softmax of key tile n0 of the current item (see fwd_bf16_kernel);
+    // masked: the tile has keys past this wave's diagonal or past the end
+    auto softmax = [&](int n0, bool masked) __attribute__((always_inline)) {
+        if (masked) {
+            // accumulator register r of key block sb holds key n0 + kofs + 4g,
+            // kofs = 32 sb + 8 (r / 4) + r % 4; it is masked when kofs > hi.
+            // The sign of hi - kofs selects -inf bit by bit (v_bfi), so no
+            // lane masks are held in scalar registers.
+            const int hi = (CAUSAL ? min(qi, S - 1) : S - 1) - (n0 + g * 4);
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kofs = sb * 32 + (r >> 2) * 8 + (r & 3);
+                    const uint32_t m = (uint32_t)((hi - kofs) >> 31);  // all ones when masked
+                    sacc[sb][r] = __uint_as_float((__float_as_uint(sacc[sb][r]) & ~m) | (0xff800000u & m));
+                }
+            }
+        }
+        float lt = exp_pack(mc);
+        if (__builtin_amdgcn_ballot_w64(!(lt <= kMaxTileSum))) {
+            float t[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t[i] = fmaxf(sacc[0][i], sacc[1][i]);
+#pragma unroll
+            for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+                for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[0]), __float_as_uint(t[0]), false, false);
+            const float mnew = fmaxf(mc, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c);
+            const float alpha = fast_exp2(mc - mnew);
+            lrow *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            mc = mnew;
+            lt = exp_pack(mc);
+        }
+        lrow += lt;
+    };
+    // O / l and lse of the current item.  O goes through this wave's Q
+    // staging area, which is free between the copy of the next item's Q into
+    // the registers (last softmax phase of this item) and the DMA of the Q
+    // after it (issued after this), so that every store writes whole rows.
+    auto epilogue = [&]() __attribute__((always_inline)) {
+        const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
+        const float ltot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+        store_rows_via_lds<D, 2>(qst, oacc, 1.0f / ltot, p.out + (row0 + qwmin) * D, S - qwmin, lane | opaque_zero());
+        if (qi < S && p.lse && g == 0) p.lse[row0 + qi] = (mc + __log2f(ltot)) * kLn2;
+    };
+    // Per item and wave: last key tile this wave sees (kact) and first key
+    // tile that needs the element mask (kmask: the diagonal tile under the
+    // causal mask, the partial last tile of a ragged sequence).
+    const int ktail = S % BN ? ntiles - 1 : ntiles;
+    // ncommon: number of key tiles k with 2 <= k < nk - 3 (the DMA's common case)
+    int kact, kmask, ncommon;
+    auto set_limits = [&]() __attribute__((always_inline)) {
+        kact = CAUSAL ? qwmax / BN : nk - 1;
+        kmask = CAUSAL ? min((qwmin + 1) / BN, ktail) : ktail;
+        ncommon = max(nk - 5, 0);
+    };
+    set_limits();
+    // V phase of position (it, k).  The rare events are tested with one range
+    // check: at an item's first tile (k = 0) the previous item's output goes
+    // out and the state restarts; at its last tile (k = nk - 1) the next
+    // item's Q rows (in LDS since two or more phases) go into the registers,
+    // after this item's last S product (previous M phase) and before the next
+    // one's first (next M phase).
+    auto vphase = [&]() __attribute__((always_inline)) {
+        if ((unsigned)(k - 1) >= (unsigned)(nk - 2)) {
+            if (k == 0) {
+                if (it > 0) {
+                    epilogue();
+                    qwmin = tile * BM + wave * 32;
+                    qwmax = qwmin + 31;
+                    qi = qwmin + l32;
+                    row0 = (int64_t)bh * S;
+                    set_limits();
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+                    mc = -1e30f;
+                    lrow = 0.f;
+                }
+            } else if (has_next) {
+                q_read();
+            }
+        }
+        if (!CAUSAL || k <= kact) {
+            softmax(k * BN, k >= kmask);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pb[i] = bf16x8{};  // see the M phase
+        }
+    };
+    // DMA at the start of phase 2n+2: K of position n+2, V of position n+1,
+    // and the next item's Q rows once the Q staging area is free: after the
+    // previous item's output has gone through it, i.e. after the V phase of
+    // the item's first tile (group 0 issues its DMA after that V phase, group
+    // 1 before it, so group 1 takes the second tile).  Buffers alternate with
+    // the position's parity: K buffer (n+2) & 1 = n & 1, V buffer (n+1) & 1.
+    // Common case (2 <= k < nk - 3): both tiles and the next iteration's
+    // inside this item, whole tiles, no Q DMA.
+    const int qdma_k = grp;
+    const uint32_t lbase = lds_addr(smem);
+    uint32_t kb_off = 0;  // (n & 1) * tile bytes
+    auto dma = [&]() __attribute__((always_inline)) {
+        const uint32_t lk = lbase + kb_off;
+        const uint32_t lv = lbase + 2u * T::BYTES + (kb_off ^ (uint32_t)T::BYTES);
+        if ((unsigned)(k - 2) < (unsigned)ncommon) {
+            kdma.issue_at(kp, true, 0, lk, wave);
+            vdma.issue_at(vp, true, 0, lv, wave);
+            kp += TSTEP;
+            vp += TSTEP;
+        } else {
+            const int kk = k + 2 < nk ? k + 2 : k + 2 - nk;  // key tiles of positions n+2, n+1
+            const int vk = k + 1 < nk ? k + 1 : 0;
+            if (k + 2 < nk || has_next) kdma.issue_at(kp, kk * BN + BN <= S, S - 1 - kk * BN, lk, wave);
+            if (k + 1 < nk || has_next) vdma.issue_at(vp, vk * BN + BN <= S, S - 1 - vk * BN, lv, wave);
+            if (k == qdma_k && has_next) q_dma(nbh, ntile);
+            // sources of the next iteration (positions n+3 and n+2)
+            kp = k + 3 == nk ? p.k + knext : kp + TSTEP;
+            vp = k + 2 == nk ? p.v + knext : vp + TSTEP;
+        }
+        kb_off ^= (uint32_t)T::BYTES;
+    };
+    int np = 0;  // parity of the position: buffers of the M phase's reads
+    // M phase of position (it, k): S of the next position and O += P V of
+    // this one, as one software pipeline.  It runs when this wave sees key
+    // tile k, or when the next position is the next item's first tile (which
+    // every wave sees): a wave past its diagonal then has P = 0 (set in its V
+    // phase), so its product adds nothing.  An S product nobody uses (past
+    // the wave's diagonal, or after the last position, on the stale but
+    // in-bounds other buffer) is harmless.
+    auto mphase = [&]() __attribute__((always_inline)) {
+        if (CAUSAL && k > kact && !(k == nk - 1 && has_next)) return;
+        __builtin_amdgcn_s_setprio(1);
+        {
+            constexpr int NQK = 2 * KS, NPV = 4 * DB, NP = NQK + NPV, AHEAD = 4;
+            const char* Kt = Kbuf(np + 1);
+            const char* Vt = Vbuf(np);
+            auto rd = [&](int i) __attribute__((always_inline)) {
+                if (i < NQK) return *(const bf16x8*)(Kt + koff[i >> 1] + (i & 1) * 32 * ROWB);
+                const int j = i - NQK;
+                const char* base = Vt + voff[j % DB] + (j / DB) * 16 * ROWB;
+                return tr_read_pair(base, base + 8 * ROWB);
+            };
+            sacc[0] = f32x16{};
+            sacc[1] = f32x16{};
+            bf16x8 buf[AHEAD];
+#pragma unroll
+            for (int i = 0; i < AHEAD; ++i) buf[i] = rd(i);
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const bf16x8 a = buf[i % AHEAD];
+                if (i + AHEAD < NP) buf[i % AHEAD] = rd(i + AHEAD);
+                if (i < NQK) {
+                    sacc[i & 1] = mfma32x32x16(a, qreg[i >> 1], sacc[i & 1]);
+                } else {
+                    const int j = i - NQK;
+                    oacc[j % DB] = mfma32x32x16(a, pb[j / DB], oacc[j % DB]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // next position; false past the last
+    auto advance = [&]() __attribute__((always_inline)) {
+        np ^= 1;
+        if (++k < nk) return true;
+        if (!has_next) return false;
+        advance_item();
+        return true;
+    };
+
+    // Phase schedule: as in fwd_bf16_kernel, over the whole stream.
+    if (grp == 0) {
+        qk(Kbuf(0));
+        phase_barrier(false);
+        do {
+            vphase();
+            phase_barrier(true);
+            dma();
+            mphase();
+            phase_barrier(false);
+        } while (advance());
+        phase_barrier(true);
+    } else {
+        phase_barrier(false);
+        qk(Kbuf(0));
+        phase_barrier(true);
+        do {
+            dma();
+            vphase();
+            phase_barrier(false);
+            mphase();
+            phase_barrier(true);
+        } while (advance());
+    }
+    epilogue();
+    if (stamping) {
+        int bh0, tile0;
+        item_bh_tile(0, bh0, tile0);
+        stamp.finish(p.stamps, bh0, tile0);
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_persist(const PersistParams& prm, uint32_t grid, hipStream_t stream) {
+    PersistParams arg = prm;
+    void* args[] = {&arg};
+    return hipLaunchKernel((const void*)&fwd_bf16_persist_kernel<D, CAUSAL>, dim3(grid), dim3(NT), args, 0, stream);
+}
+
+// Compute units of the stream's device (cached per device).
+int device_cus(hipStream_t stream) {
+    static int cus[kMaxDevices] = {};
+    int dev = 0;
+    if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return 0;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <int D, bool CAUSAL, bool LOCAL = false, bool BLOCK = false, bool SPLIT = false>
 hipError_t launch(const Params& prm, hipStream_t stream) {
     Params arg = prm;
@@ -696,6 +1180,33 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     // a window of at least S keys hides nothing the causal mask shows
     if (a.causal && a.window > 0 && a.window < a.S)
         return a.D == 128 ? launch<128, true, true>(prm, stream) : launch<64, true, true>(prm, stream);
+    // Persistent form: plain attention, every item at least one 256-query
+    // tile long (so each has 4 or more key tiles), causal query tiles in
+    // pairs, and whole rounds of units over the compute units.
+    if (!a.bmask && !windowed && !split && a.S >= BM && !(a.causal && prm.nq % 2)) {
+        const int cus = device_cus(stream);
+        const int64_t units = (int64_t)a.B * a.Hq * (a.causal ? prm.nq / 2 : prm.nq);
+        if (cus >= 8 && cus % 8 == 0 && units % cus == 0 && units / cus <= (1 << 20)) {
+            PersistParams pp;
+            pp.q = prm.q;
+            pp.k = prm.k;
+            pp.v = prm.v;
+            pp.out = prm.out;
+            pp.lse = prm.lse;
+            pp.Hq = prm.Hq;
+            pp.Hkv = prm.Hkv;
+            pp.S = prm.S;
+            pp.group = prm.group;
+            pp.nq = prm.nq;
+            pp.units = a.causal ? prm.nq / 2 : prm.nq;
+            pp.rounds = (int)(units / cus);
+            pp.c = prm.c;
+            pp.stamps = prm.stamps;
+            if (a.D == 128)
+                return a.causal ? launch_persist<128, true>(pp, cus, stream) : launch_persist<128, false>(pp, cus, stream);
+            return a.causal ? launch_persist<64, true>(pp, cus, stream) : launch_persist<64, false>(pp, cus, stream);
+        }
+    }
     if (split) {
         if (a.D == 128)
             return a.causal ? launch<128, true, false, false, true>(prm, stream)

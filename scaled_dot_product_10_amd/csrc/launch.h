@@ -26,6 +26,8 @@ struct FwdArgs {
 };
 
 constexpr int kStampWords = 8;
+// GPUs of one process with per-device cached state (for example CU counts)
+constexpr int kMaxDevices = 64;
 // Workgroups a bf16 forward launch may use (stamp records to provide).
 int64_t fwd_bf16_max_workgroups(int B, int Hq, int S);
 

@@ -86,7 +86,7 @@ struct TrOffsets {
 // rows share one 256-byte bank line), with its two 8-byte halves swapped for
 // rows 16-31: the 32 lanes of one write (one row each, same chunk and half)
 // then cover all 64 banks once, and the reads (16 lanes per 256 bytes) too.
-template <int D>
+template <int D, int BATCH = 32 * D * 2 / 16 / 64>
 __device__ __forceinline__ void store_rows_via_lds(char* stage, const f32x16 (&acc)[D / 32], float scale,
                                                    uint16_t* dst, int nrows, int lane) {
     constexpr int RB = D * 2;     // bytes per row
@@ -104,13 +104,19 @@ __device__ __forceinline__ void store_rows_via_lds(char* stage, const f32x16 (&a
             *(u32x2*)(stage + l32 * RB + ((c ^ wswz) * 16) + whalf * 8) = w;
         }
     }
-    // the wave's own LDS writes complete before its reads (in order)
+    // the wave's own LDS writes complete before its reads (in order).  BATCH
+    // read-backs are in flight at a time (fewer registers for callers that
+    // hold much else).
 #pragma unroll
-    for (int i = 0; i < 32 * CPO / 64; ++i) {
-        const int pos = i * 64 + lane, r = pos / CPO, c = pos % CPO;
-        u32x4 x = *(const u32x4*)(stage + r * RB + ((c ^ ((r / RPL) % CPO)) * 16));
-        if ((r >> 4) & 1) x = u32x4{x[2], x[3], x[0], x[1]};
-        if (r < nrows) *(u32x4*)(dst + (int64_t)r * D + c * 8) = x;
+    for (int i0 = 0; i0 < 32 * CPO / 64; i0 += BATCH) {
+#pragma unroll
+        for (int i = i0; i < i0 + BATCH; ++i) {
+            const int pos = i * 64 + lane, r = pos / CPO, c = pos % CPO;
+            u32x4 x = *(const u32x4*)(stage + r * RB + ((c ^ ((r / RPL) % CPO)) * 16));
+            if ((r >> 4) & 1) x = u32x4{x[2], x[3], x[0], x[1]};
+            if (r < nrows) *(u32x4*)(dst + (int64_t)r * D + c * 8) = x;
+        }
+        if (i0 + BATCH < 32 * CPO / 64) __builtin_amdgcn_sched_barrier(0);
     }
 }
 

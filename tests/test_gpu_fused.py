@@ -188,19 +188,11 @@ def test_large_logits(orc, dtype):
     G.check_close(f"large logits {dtype}", G.host(out), ref_o, dtype, G.host(lse), ref_l, lse_tol=lse_tol)
 
 
-@pytest.mark.parametrize("name,causal", [("C3", True), ("C2", True), ("C3", False)])
-def test_stamped_launch(name, causal):
-    """The stamped launch runs the same kernel: bit-identical results; every
-    workgroup of the grid leaves one record, the records cover each
-    (head, query tile) once, and the counters advance."""
+def _stamped(dq, dk, dv, B, Hq, Hkv, S, D, sc, causal):
     from scaled_dot_product_10_amd import _lib
 
-    c, q, k, v, dq, dk, dv = workload(name)
-    B, Hq, Hkv, S, D = c["B"], c["Hq"], c["Hkv"], c["S"], c["D"]
-    sc = 1.0 / math.sqrt(D)
-    out0, lse0 = api.fwd(dq, dk, dv, causal=causal, scale=sc)
-    out = torch.empty_like(out0)
-    lse = torch.empty_like(lse0)
+    out = torch.empty_like(dq)
+    lse = torch.empty((B, Hq, S), device=dq.device, dtype=torch.float32)
     nrec = _lib.attn_fwd_bf16_stamp_bytes(B, Hq, S) // 64
     st = torch.zeros((nrec, 8), dtype=torch.int64, device=dq.device)
     rc = _lib.attn_fwd_bf16_stamped(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -208,19 +200,79 @@ def test_stamped_launch(name, causal):
                                     torch.cuda.current_stream().cuda_stream)
     assert rc == 0
     torch.cuda.synchronize()
-    assert torch.equal(out, out0) and torch.equal(lse, lse0)
     rec = st.cpu().numpy()
     used = rec[:, 1] != 0
     n = int(used.sum())
     assert used[:n].all(), "records must be the first n slots (one per workgroup)"
-    rec = rec[:n]
-    qt = (S + n // (B * Hq) - 1) // (n // (B * Hq))  # queries per workgroup
-    assert n == B * Hq * ((S + qt - 1) // qt) and qt in (128, 256)
+    return out, lse, rec[:n]
+
+
+def _persistent(B, Hq, S, causal):
+    """Whether the launch takes the persistent schedule: one workgroup per
+    compute unit over whole rounds of units (causal: pairs of query tiles)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nq = (S + 255) // 256
+    split = S > 256 and B * Hq * nq <= (256 if causal else 128)  # the key-split form
+    if split or S < 256 or (causal and nq % 2):
+        return False
+    units = B * Hq * (nq // 2 if causal else nq)
+    return units % cus == 0
+
+
+@pytest.mark.parametrize("name,causal", [("C3", True), ("C2", True), ("C3", False)])
+def test_stamped_launch(name, causal):
+    """The stamped launch runs the same kernel: bit-identical results; every
+    workgroup leaves one record (one per (head, query tile), or one per
+    compute unit for the persistent schedule, then naming its first item),
+    and the counters advance."""
+    c, q, k, v, dq, dk, dv = workload(name)
+    B, Hq, Hkv, S, D = c["B"], c["Hq"], c["Hkv"], c["S"], c["D"]
+    sc = 1.0 / math.sqrt(D)
+    out0, lse0 = api.fwd(dq, dk, dv, causal=causal, scale=sc)
+    out, lse, rec = _stamped(dq, dk, dv, B, Hq, Hkv, S, D, sc, causal)
+    assert torch.equal(out, out0) and torch.equal(lse, lse0)
+    n = rec.shape[0]
     pairs = set(zip(rec[:, 6].tolist(), rec[:, 7].tolist()))
-    assert pairs == {(bh, t) for bh in range(B * Hq) for t in range(n // (B * Hq))}
+    assert len(pairs) == n
+    if _persistent(B, Hq, S, causal):
+        assert n == torch.cuda.get_device_properties(0).multi_processor_count
+    else:
+        qt = (S + n // (B * Hq) - 1) // (n // (B * Hq))  # queries per workgroup
+        assert n == B * Hq * ((S + qt - 1) // qt) and qt in (128, 256)
+        assert pairs == {(bh, t) for bh in range(B * Hq) for t in range(n // (B * Hq))}
     dt = rec[:, 2] - rec[:, 0]
     dr = rec[:, 3] - rec[:, 1]
     assert (dt > 0).all() and (dr > 0).all()
     ghz = dt.sum() / dr.sum() * 0.1  # real-time counter at 100 MHz
     G.report(f"stamped {name} causal={causal}", workgroups=n, sclk_ghz=float(ghz))
     assert 0.3 < ghz < 3.0
+
+
+# The persistent schedule (one workgroup per compute unit running a list of
+# query tiles back to back, the key/value stream continuing across them):
+# shapes whose unit count is a multiple of the 256 compute units, ragged S,
+# D 64 and 128, GQA, one and several rounds; every element compared.
+PERSIST = [
+    (1, 64, 8, 2000, 64, True), (2, 64, 16, 1000, 128, True), (4, 64, 16, 1000, 128, True),
+    (1, 32, 4, 2000, 128, False), (2, 128, 32, 300, 64, False), (1, 256, 256, 256, 128, False),
+]
+
+
+@pytest.mark.parametrize("shape", PERSIST, ids=lambda s: "B{}H{}kv{}S{}D{}c{}".format(*s))
+def test_persistent_schedule_full_compare(orc, shape):
+    B, Hq, Hkv, S, D, causal = shape
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", seed=600 + S + D + Hq)
+    sc = 1.0 / math.sqrt(D)
+    dq, dk, dv = G.dev(q), G.dev(k), G.dev(v)
+    out, lse = api.fwd(dq, dk, dv, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    assert _persistent(B, Hq, S, causal)
+    # the stamped launch shows the schedule taken: one record per compute unit
+    out2, lse2, rec = _stamped(dq, dk, dv, B, Hq, Hkv, S, D, sc, causal)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    assert rec.shape[0] == torch.cuda.get_device_properties(0).multi_processor_count
+    ref_o, ref_l = orc.attn_fwd(q.f32, k.f32, v.f32, sc, causal)
+    G.check_close(f"persistent {shape}", G.host(out), ref_o, "bf16", G.host(lse), ref_l, keys=S)
+    if causal:
+        g = Hq // Hkv
+        assert torch.equal(out[:, :, 0, :], dv[:, :, 0, :].repeat_interleave(g, dim=1))
