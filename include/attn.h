@@ -76,7 +76,9 @@ typedef enum attn_status {
     ATTN_ERR_BAD_SCALE = 4,    /* scale is not finite, or not > 0                     */
     ATTN_ERR_MISALIGNED = 5,   /* a tensor pointer breaks the alignment rule          */
     ATTN_ERR_ALIAS = 6,        /* an output overlaps an input                         */
-    ATTN_ERR_HIP = 7           /* the HIP launch failed; see attn_last_hip_error()    */
+    ATTN_ERR_HIP = 7,          /* the HIP launch failed; see attn_last_hip_error()    */
+    ATTN_ERR_TOO_LARGE = 8     /* the call needs more than the library's fixed       */
+                               /* scratch (allocation-free entry points only)         */
 } attn_status;
 
 /* ---------------------------------------------------------------------------
@@ -209,6 +211,27 @@ size_t attn_splitkv_workspace_bytes(int B, int Hq, int Sq, int D, int nsplit);
  * bad size. */
 int attn_splitkv_default_splits(int B, int Hq, int Hkv, int Sq, int Skv);
 
+/* ---------------------------------------------------------------------------
+ * Split-KV forward that allocates nothing (bfloat16).
+ *
+ * For callers that cannot allocate device memory at call time: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same operation, arguments, results and kernels as attn_fwd_splitkv_bf16,
+ * without the workspace argument: the partial results live in a scratch
+ * array of attn_splitkv_noalloc_max_bytes() bytes (16 MiB) that the library
+ * holds on every GPU it runs on until the process ends.  A call whose
+ * workspace (attn_splitkv_workspace_bytes) would exceed it returns
+ * ATTN_ERR_TOO_LARGE and launches nothing.  No hipMalloc or hipFree; the
+ * first call on a GPU looks up that GPU's scratch address once.  Calls that
+ * overlap on one GPU (on different streams, or from several host threads)
+ * share the scratch and race: serialise them.  Two kernel launches.
+ * ------------------------------------------------------------------------- */
+attn_status attn_fwd_splitkv_bf16_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                                          int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                                          int causal, int nsplit, void* stream);
+/* Bytes of the scratch behind attn_fwd_splitkv_bf16_noalloc (the largest
+ * workspace it serves). */
+size_t attn_splitkv_noalloc_max_bytes(void);
 
 /* ---------------------------------------------------------------------------
  * Unfused trio, mirroring the naive pipeline one step per kernel.

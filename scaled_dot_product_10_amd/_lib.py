@@ -22,6 +22,7 @@ STATUS = {
     5: "ATTN_ERR_MISALIGNED",
     6: "ATTN_ERR_ALIAS",
     7: "ATTN_ERR_HIP",
+    8: "ATTN_ERR_TOO_LARGE",
 }
 
 _p = ctypes.c_void_p
@@ -47,6 +48,8 @@ SIGNATURES = {
     "attn_fwd_splitkv_bf16": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _i, _p]),
     "attn_splitkv_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "attn_splitkv_default_splits": (_i, [_i, _i, _i, _i, _i]),
+    "attn_fwd_splitkv_bf16_noalloc": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _i, _p]),
+    "attn_splitkv_noalloc_max_bytes": (ctypes.c_size_t, []),
     "attn_bwd_bf16": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i]),
     "attn_scores_bytes": (ctypes.c_size_t, [_i, _i, _i]),
@@ -155,6 +158,15 @@ def attn_splitkv_workspace_bytes(B, Hq, Sq, D, nsplit) -> int:
 
 def attn_splitkv_default_splits(B, Hq, Hkv, Sq, Skv) -> int:
     return int(lib().attn_splitkv_default_splits(B, Hq, Hkv, Sq, Skv))
+
+
+def attn_fwd_splitkv_bf16_noalloc(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, nsplit, stream) -> int:
+    return _call("attn_fwd_splitkv_bf16_noalloc", q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, nsplit,
+                 stream)
+
+
+def attn_splitkv_noalloc_max_bytes() -> int:
+    return int(lib().attn_splitkv_noalloc_max_bytes())
 
 
 def attn_bwd_bf16(q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, S, D, scale, causal, stream) -> int:

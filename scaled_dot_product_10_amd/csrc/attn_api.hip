@@ -436,6 +436,22 @@ attn_status attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, v
         (hipStream_t)stream));
 }
 
+attn_status attn_fwd_splitkv_bf16_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                                          int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                                          int nsplit, void* stream) {
+    const attn_status st =
+        check_splitkv(q, k, v, out, lse, nullptr, B, Hq, Hkv, Sq, Skv, D, scale, causal, nsplit);
+    if (st != ATTN_OK) return st;
+    if (splitkv_ws_floats(B, Hq, Sq, D, nsplit) > attn::kSplitkvScratchFloats) return ATTN_ERR_TOO_LARGE;
+    float* ws = nullptr;
+    const hipError_t e = attn::splitkv_scratch((hipStream_t)stream, &ws);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(attn::launch_splitkv_bf16(
+        splitkv_args(q, k, v, out, lse, ws, B, Hq, Hkv, Sq, Skv, D, scale, causal, nsplit), (hipStream_t)stream));
+}
+
+size_t attn_splitkv_noalloc_max_bytes(void) { return (size_t)attn::kSplitkvScratchFloats * 4; }
+
 size_t attn_splitkv_workspace_bytes(int B, int Hq, int Sq, int D, int nsplit) {
     if (nsplit < 1 || nsplit > kMaxSplits || (D != 64 && D != 128)) return 0;
     const int64_t n = splitkv_ws_floats(B, Hq, Sq, D, nsplit);
@@ -505,6 +521,7 @@ const char* attn_status_str(attn_status s) {
         case ATTN_ERR_MISALIGNED: return "ATTN_ERR_MISALIGNED: tensors need 16-byte alignment (lse 4)";
         case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS: an output overlaps an input";
         case ATTN_ERR_HIP: return "ATTN_ERR_HIP: kernel launch failed";
+        case ATTN_ERR_TOO_LARGE: return "ATTN_ERR_TOO_LARGE: the call needs more than the library's fixed scratch";
     }
     return "unknown attn_status";
 }

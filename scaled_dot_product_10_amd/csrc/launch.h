@@ -105,6 +105,10 @@ hipError_t launch_pv_gemm_bf16(const PvArgs& a, hipStream_t stream);
 hipError_t launch_pv_gemm_f32(const PvArgs& a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);          // three kernels
 hipError_t launch_splitkv_bf16(const SplitKvArgs& a, hipStream_t stream);  // two kernels
+// Allocation-free split-KV: floats of the library's per-GPU scratch (16 MiB),
+// and its device address on the stream's GPU (looked up on first use there).
+constexpr int64_t kSplitkvScratchFloats = int64_t(4) << 20;
+hipError_t splitkv_scratch(hipStream_t stream, float** ptr);
 int splitkv_row_blocks(int Hq, int Hkv, int Sq);  // workgroups per (b, kv head) and split
 int splitkv_chunk();                              // keys per workgroup step
 

@@ -22,6 +22,8 @@
 //   at the end.  The kernel is bound by the K/V read: its arithmetic is a
 //   small fraction of the matrix cores' rate.
 // splitkv_merge_kernel: one workgroup per row.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 #include "lds_tiles.h"
@@ -290,7 +292,42 @@ hipError_t launch1(K kernel, uint32_t grid, const P& prm, hipStream_t stream) {
     return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(NT), args, 0, stream);
 }
 
+// Scratch of the allocation-free entry point: the partial outputs and
+// log-sum-exps of every split, in the layout of the caller's workspace.  One
+// copy per GPU, held for the life of the process; every call on a GPU
+// shares it (concurrent calls on one GPU race).  Each call's split kernel
+// writes every slot its merge reads, so nothing needs clearing between calls.
+static __device__ __align__(256) float scratch[kSplitkvScratchFloats];
+
 }  // namespace
+
+// Device address of this GPU's scratch: looked up once per device (with that
+// device current) and kept; the array's host-side name is not a device
+// address and must never reach a kernel.
+hipError_t splitkv_scratch(hipStream_t stream, float** ptr) {
+    static std::mutex mu;
+    static float* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (e2 != hipSuccess) return e2;
+        if (!a) return hipErrorInvalidSymbol;
+        addr[dev] = (float*)a;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 int splitkv_row_blocks(int Hq, int Hkv, int Sq) { return (Hq / Hkv * Sq + ROWS - 1) / ROWS; }
 int splitkv_chunk() { return CHUNK; }

@@ -40,7 +40,7 @@ def L():
 
 def test_header_symbols_are_exported(L):
     syms = header_symbols()
-    assert len(syms) == 22, syms
+    assert len(syms) == 24, syms
     nm = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)], capture_output=True, text=True,
                         check=True).stdout
     exported = set(re.findall(r"\bT (\w+)$", nm, flags=re.M))
@@ -176,6 +176,38 @@ def test_blockmask_rejects():
     assert call(mask=E + 8) == ALIAS     # inside lse
     assert call(mask=Dp - 10, sb=0, sh=0) == ALIAS  # 25 flags (5 x 5 blocks) reach into out
     assert call(out=Bp) == ALIAS
+
+
+def test_splitkv_noalloc_rejects():
+    """The allocation-free split-KV takes the same checks (no workspace
+    argument) and refuses, before any HIP call, a call whose partial results
+    would not fit the library's fixed scratch."""
+    f = _lib.attn_fwd_splitkv_bf16_noalloc
+    TOO_LARGE = 8
+
+    def call(**kw):
+        a = dict(q=A, k=Bp, v=C, out=Dp, lse=E, B=1, Hq=4, Hkv=2, Sq=1, Skv=100, D=128, scale=0.1, causal=1,
+                 nsplit=4, stream=None)
+        a.update(kw)
+        return f(*[a[n] for n in ("q", "k", "v", "out", "lse", "B", "Hq", "Hkv", "Sq", "Skv", "D", "scale",
+                                  "causal", "nsplit", "stream")])
+
+    cap = _lib.attn_splitkv_noalloc_max_bytes()
+    assert cap == 16 << 20
+    assert call(q=None) == NULL
+    assert call(out=None) == NULL
+    assert call(Sq=101) == SHAPE
+    assert call(Hq=3) == SHAPE
+    assert call(D=80) == UNSUP
+    assert call(nsplit=0) == UNSUP
+    assert call(scale=0.0) == SCALE
+    assert call(lse=E + 2) == ALIGN
+    assert call(out=A) == ALIAS
+    # 64 x 64 rows x 129 floats x 16 splits = 33.8 MB > 16 MiB
+    assert _lib.attn_splitkv_workspace_bytes(1, 64, 64, 128, 16) > cap
+    assert call(Hq=64, Hkv=8, Sq=64, Skv=4096, nsplit=16) == TOO_LARGE
+    assert _lib.STATUS[TOO_LARGE] == "ATTN_ERR_TOO_LARGE"
+    assert _lib.attn_status_str(TOO_LARGE).startswith("ATTN_ERR_TOO_LARGE")
 
 
 def test_splitkv_rejects_and_sizes():
