@@ -664,11 +664,11 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
 //
 // Items: each head's query tiles form units; causal: unit j = tiles nq-1-j
 // and j (a long and a short item with 4 (nq + 1) key tiles together, so every
-// unit is equally long); full: unit j = tile j.  Workgroup w runs unit
-// r G + (w % 8) G/8 + w / 8 in round r: workgroups on one XCD (the hardware
-// deals them round-robin over the 8 XCDs) take consecutive units, i.e. the
-// tiles of a few heads, whose key/value tiles they read in step through the
-// XCD's L2.
+// unit is equally long; the short one runs its key tiles in descending
+// order); full: unit j = tile j.  Workgroup w runs unit r G + (w % 8) G/8 +
+// w / 8 in round r: workgroups on one XCD (the hardware deals them
+// round-robin over the 8 XCDs) take consecutive units, i.e. the tiles of a
+// few heads, whose key/value tiles they read in step through the XCD's L2.
 struct PersistParams {
     const uint16_t* q;
     const uint16_t* k;
@@ -689,6 +689,14 @@ struct PersistParams {
 __device__ __forceinline__ int opaque_zero() {
     int z;
     asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+// The same for wave-uniform values: values used only at item boundaries are
+// recomputed there from S | opaque_szero() instead of being held in scalar
+// registers across the loop.
+__device__ __forceinline__ int opaque_szero() {
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
     return z;
 }
 
@@ -715,29 +723,35 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     const int g = lane >> 5;
     char* const qst = smem + 4 * T::BYTES + wave * QWB;  // this wave's Q rows (K-tile layout)
     const int S = p.S;
-    const int ntiles = (S + BN - 1) / BN;
     const int nitems = p.rounds * (CAUSAL ? 2 : 1);
     const uint32_t G = gridDim.x;
     // XCD x (blockIdx % 8) runs units [x U/8, (x+1) U/8) of all U = rounds G:
     // consecutive heads, G/8 units per round
-    const uint32_t xbase = (blockIdx.x % 8u) * (uint32_t)p.rounds * (G / 8u) + blockIdx.x / 8u;
 
     // item i of this workgroup -> (b * Hq + h, query tile); key tiles it runs
     auto item_bh_tile = [&](int i, int& bh, int& tile) __attribute__((always_inline)) {
         const int r = CAUSAL ? i >> 1 : i;
-        const uint32_t L = xbase + (uint32_t)r * (G / 8u);
+        const uint32_t w = blockIdx.x | (uint32_t)opaque_szero();
+        const uint32_t L = ((w % 8u) * (uint32_t)p.rounds + (uint32_t)r) * (G / 8u) + w / 8u;
         bh = (int)(L / (uint32_t)p.units);
         const int j = (int)(L % (uint32_t)p.units);
         tile = CAUSAL ? ((i & 1) ? j : p.nq - 1 - j) : j;
     };
     auto item_tiles = [&](int tile) __attribute__((always_inline)) {
-        return CAUSAL ? min(ntiles, (min(tile * BM + BM, S) - 1) / BN + 1) : ntiles;
+        const int Sx = S | opaque_szero(), nt = (Sx + BN - 1) / BN;
+        return CAUSAL ? min(nt, (min(tile * BM + BM, Sx) - 1) / BN + 1) : nt;
     };
-    // The stream position: key tile k of the current item (nk key tiles,
-    // head bh, query tile); the next item's head and query tile.  Every item
-    // has at least 4 key tiles, so the two positions after the current one
-    // lie in these two items.
-    int it = 0, k = 0, nk, bh, tile;
+    // The stream position: position k of the current item (nk key tiles,
+    // head bh, query tile), at key tile kt, moving by dk; the next item's
+    // head, query tile, key tile count and direction.  Every item has at
+    // least 4 key tiles, so the two positions after the current one lie in
+    // these two items.  The second item of a causal pair runs its key tiles
+    // in descending order: pair j's second item starts when its first ends,
+    // at a time that depends on j, but it then reads at every moment the
+    // same key tile as the second items of the head's other pairs, so a
+    // head's workgroups read at most two key tiles at a time (the ascending
+    // and the descending front) and the XCD's L2 serves the other reads.
+    int it = 0, k = 0, nk, bh, tile, kt = 0, dk = 1;  // the next item's direction: CAUSAL ? -dk : dk
     int nbh = 0, ntile = 0;
     auto kv_of = [&](int bh_) __attribute__((always_inline)) {
         const int b = bh_ / p.Hq, h = bh_ % p.Hq;
@@ -748,23 +762,35 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     bool has_next = nitems > 1;
     if (has_next) item_bh_tile(1, nbh, ntile);
     // DMA sources: K of position n+2 and V of position n+1 (tile pointers
-    // that advance one tile per position and jump to the next item's first
-    // key at the crossing), and their key tiles within their items
+    // that move one tile per position, cstep bytes in the current item and
+    // CAUSAL ? -cstep : cstep in the next, and jump to the next item's first
+    // key tile at the crossing)
     constexpr int64_t TSTEP = (int64_t)BN * D;  // elements per key tile
     const int64_t kv0 = kv_of(bh);
-    int64_t knext = has_next ? kv_of(nbh) : 0;  // next item's key 0
-    const uint16_t* kp = p.k + kv0 + 2 * TSTEP;
-    const uint16_t* vp = p.v + kv0 + TSTEP;
+    int64_t cstep = TSTEP * 2;
+    // element offset of the next item's first key tile (the last one when it
+    // runs in descending order)
+    auto first_tile = [&]() __attribute__((always_inline)) {
+        return kv_of(nbh) + (CAUSAL && dk > 0 ? (int64_t)(item_tiles(ntile) - 1) * TSTEP : 0);
+    };
+    int64_t knext = has_next ? first_tile() : 0;
+    const char* kp = (const char*)(p.k + kv0 + 2 * TSTEP);
+    const char* vp = (const char*)(p.v + kv0 + TSTEP);
     auto advance_item = [&]() __attribute__((always_inline)) {
         ++it;
         bh = nbh;
         tile = ntile;
         nk = item_tiles(tile);
+        if (CAUSAL) {
+            dk = -dk;
+            cstep = -cstep;
+        }
         k = 0;
+        kt = dk < 0 ? nk - 1 : 0;
         has_next = it + 1 < nitems;
         if (has_next) {
             item_bh_tile(it + 1, nbh, ntile);
-            knext = kv_of(nbh);
+            knext = first_tile();
         }
     };
 
@@ -823,9 +849,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     const float c = p.c;
     // the item whose softmax and output this wave is on
     int qwmin = tile * BM + wave * 32;
-    int qwmax = qwmin + 31;
     int qi = qwmin + l32;
-    int64_t row0 = (int64_t)bh * S;
+    int wbh = bh;
     f32x16 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
@@ -938,17 +963,22 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     auto epilogue = [&]() __attribute__((always_inline)) {
         const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
         const float ltot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+        const int64_t row0 = (int64_t)wbh * S;
         store_rows_via_lds<D, 2>(qst, oacc, 1.0f / ltot, p.out + (row0 + qwmin) * D, S - qwmin, lane | opaque_zero());
         if (qi < S && p.lse && g == 0) p.lse[row0 + qi] = (mc + __log2f(ltot)) * kLn2;
     };
     // Per item and wave: last key tile this wave sees (kact) and first key
     // tile that needs the element mask (kmask: the diagonal tile under the
-    // causal mask, the partial last tile of a ragged sequence).
-    const int ktail = S % BN ? ntiles - 1 : ntiles;
-    // ncommon: number of key tiles k with 2 <= k < nk - 3 (the DMA's common case)
+    // causal mask, the partial last tile of a ragged sequence).  Every row
+    // of the wave sees the first key of each tile up to kact, so a
+    // descending item's first tile already gives every row a finite max.
+    // ncommon: number of positions k with 2 <= k < nk - 3 (the DMA's common
+    // case: whole tiles in this item)
     int kact, kmask, ncommon;
     auto set_limits = [&]() __attribute__((always_inline)) {
-        kact = CAUSAL ? qwmax / BN : nk - 1;
+        kact = CAUSAL ? (qwmin + 31) / BN : nk - 1;
+        const int Sx = S | opaque_szero();
+        const int ktail = Sx / BN;  // the partial last key tile, or one past the last
         kmask = CAUSAL ? min((qwmin + 1) / BN, ktail) : ktail;
         ncommon = max(nk - 5, 0);
     };
@@ -965,9 +995,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
                 if (it > 0) {
                     epilogue();
                     qwmin = tile * BM + wave * 32;
-                    qwmax = qwmin + 31;
                     qi = qwmin + l32;
-                    row0 = (int64_t)bh * S;
+                    wbh = bh;
                     set_limits();
 #pragma unroll
                     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
@@ -978,8 +1007,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
                 q_read();
             }
         }
-        if (!CAUSAL || k <= kact) {
-            softmax(k * BN, k >= kmask);
+        if (!CAUSAL || kt <= kact) {
+            softmax(kt * BN, kt >= kmask);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) pb[i] = bf16x8{};  // see the M phase
@@ -1000,32 +1029,42 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
         const uint32_t lk = lbase + kb_off;
         const uint32_t lv = lbase + 2u * T::BYTES + (kb_off ^ (uint32_t)T::BYTES);
         if ((unsigned)(k - 2) < (unsigned)ncommon) {
-            kdma.issue_at(kp, true, 0, lk, wave);
-            vdma.issue_at(vp, true, 0, lv, wave);
-            kp += TSTEP;
-            vp += TSTEP;
+            kdma.issue_at((const uint16_t*)kp, true, 0, lk, wave);
+            vdma.issue_at((const uint16_t*)vp, true, 0, lv, wave);
+            kp += cstep;
+            vp += cstep;
         } else {
-            const int kk = k + 2 < nk ? k + 2 : k + 2 - nk;  // key tiles of positions n+2, n+1
-            const int vk = k + 1 < nk ? k + 1 : 0;
-            if (k + 2 < nk || has_next) kdma.issue_at(kp, kk * BN + BN <= S, S - 1 - kk * BN, lk, wave);
-            if (k + 1 < nk || has_next) vdma.issue_at(vp, vk * BN + BN <= S, S - 1 - vk * BN, lv, wave);
+            // key tiles of positions n+2 and n+1, in this item or the next
+            const int kn = k + 2 - nk;
+            const bool ndesc = CAUSAL && dk > 0;
+            const int nnk = ndesc ? item_tiles(ntile) : 0;
+            const int kk = kn < 0 ? kt + 2 * dk : (ndesc ? nnk - 1 - kn : kn);
+            const int vk = k + 1 < nk ? kt + dk : (ndesc ? nnk - 1 : 0);
+            if (k + 2 < nk || has_next)
+                kdma.issue_at((const uint16_t*)kp, kk * BN + BN <= S, S - 1 - kk * BN, lk, wave);
+            if (k + 1 < nk || has_next)
+                vdma.issue_at((const uint16_t*)vp, vk * BN + BN <= S, S - 1 - vk * BN, lv, wave);
             if (k == qdma_k && has_next) q_dma(nbh, ntile);
             // sources of the next iteration (positions n+3 and n+2)
-            kp = k + 3 == nk ? p.k + knext : kp + TSTEP;
-            vp = k + 2 == nk ? p.v + knext : vp + TSTEP;
+            const int64_t nstep = CAUSAL ? -cstep : cstep;
+            kp = k + 3 < nk ? kp + cstep : (k + 3 == nk ? (const char*)(p.k + knext) : kp + nstep);
+            vp = k + 2 < nk ? vp + cstep : (k + 2 == nk ? (const char*)(p.v + knext) : vp + nstep);
         }
         kb_off ^= (uint32_t)T::BYTES;
     };
     int np = 0;  // parity of the position: buffers of the M phase's reads
     // M phase of position (it, k): S of the next position and O += P V of
     // this one, as one software pipeline.  It runs when this wave sees key
-    // tile k, or when the next position is the next item's first tile (which
-    // every wave sees): a wave past its diagonal then has P = 0 (set in its V
-    // phase), so its product adds nothing.  An S product nobody uses (past
-    // the wave's diagonal, or after the last position, on the stale but
-    // in-bounds other buffer) is harmless.
+    // tile kt, when it sees the next position's tile (a descending item's
+    // position before the first tile the wave sees), or at an item's last
+    // position when another item follows: a wave that does not see tile kt
+    // has P = 0 (set in its V phase), so its product adds nothing.  An S
+    // product nobody uses (a tile the wave does not see, or after the last
+    // position, on the stale but in-bounds other buffer) is harmless.
     auto mphase = [&]() __attribute__((always_inline)) {
-        if (CAUSAL && k > kact && !(k == nk - 1 && has_next)) return;
+        // descending items also need the M phase of the position before the
+        // first tile the wave sees (kact + 1), for that tile's S product
+        if (CAUSAL && kt > kact - (dk >> 1) && !(k == nk - 1 && has_next)) return;
         __builtin_amdgcn_s_setprio(1);
         {
             constexpr int NQK = 2 * KS, NPV = 4 * DB, NP = NQK + NPV, AHEAD = 4;
@@ -1060,6 +1099,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     // next position; false past the last
     auto advance = [&]() __attribute__((always_inline)) {
         np ^= 1;
+        kt += dk;
         if (++k < nk) return true;
         if (!has_next) return false;
         advance_item();
