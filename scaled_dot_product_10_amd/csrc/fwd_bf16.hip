@@ -272,6 +272,15 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     int nend = SPLIT ? (nall + 1) / 2 : nall;
     const int toff = SPLIT && grp ? nend : 0;
     const int nbeg = LOCAL ? max(0, m0 - p.window + 1) / BN : 0;
+    // LOCAL: the workgroup's key tiles nbeg .. nend-1 run in rotated order,
+    // position nbeg + i taking tile nbeg + (i + rot) mod cnt with rot such
+    // that the tile is congruent to i modulo cnt.  Workgroups whose windows
+    // have the same length (all but the first few query tiles) and that
+    // start together then read the same key tile at the same time wherever
+    // their windows overlap, so their K/V reads meet in the XCD's L2 (in
+    // ascending order neighbouring query tiles would be four tiles apart).
+    const int lcnt = LOCAL ? nend - nbeg : 1;
+    const int lrot = LOCAL ? (lcnt - nbeg % lcnt) % lcnt : 0;
 
     if (BLOCK) {
         // list the tiles below nend that a query block of this workgroup may
@@ -323,6 +332,12 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     // once per loop iteration; the key tile it names, and whether this wave's
     // query block may see that tile.
     auto ent = [&](int n) __attribute__((always_inline)) {
+        if (LOCAL) {
+            int i = n - nbeg + lrot;  // < 2 lcnt + 2 for the positions the loop names
+            i -= i >= lcnt ? lcnt : 0;
+            i -= i >= lcnt ? lcnt : 0;
+            return (uint32_t)(nbeg + i);
+        }
         return BLOCK ? __builtin_amdgcn_readfirstlane(blist[n]) : (uint32_t)(n + toff);
     };
     auto tile_of = [&](uint32_t e) __attribute__((always_inline)) { return BLOCK ? (int)(e & 0xffffffu) : (int)e; };
@@ -516,9 +531,11 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     // path: for the last tile the S(n+1) product reads the (stale, in-bounds)
     // other K buffer and its result is never used.
     auto mphase = [&](int n, uint32_t e0, uint32_t e1) __attribute__((always_inline)) {
-        if (!active(e0)) return;
-        if (LOCAL && !in_window(e0)) {  // P(n) is all zero here: only S(n+1), if it counts
-            if (in_window(e1)) qk(Kbuf(n + 1));
+        // P(n) is all zero for a tile this wave does not see: only S(n+1), if
+        // it counts (LOCAL's rotated order puts such tiles anywhere; in
+        // ascending order a tile past the diagonal is followed by no other)
+        if (!active(e0) || (LOCAL && !in_window(e0))) {
+            if (LOCAL && active(e1) && in_window(e1)) qk(Kbuf(n + 1));
             return;
         }
         constexpr int NQK = 2 * KS, NPV = 4 * DB, NP = NQK + NPV, AHEAD = 4;

@@ -31,6 +31,8 @@ CASES = [
     ((1, 2, 2, 200, 128), 64), ((1, 2, 2, 200, 128), 65), ((2, 4, 2, 333, 128), 100), ((1, 2, 1, 640, 128), 255),
     ((1, 2, 1, 640, 128), 256), ((1, 2, 1, 640, 128), 257), ((1, 3, 3, 1000, 64), 300), ((1, 2, 2, 1000, 128), 999),
     ((1, 1, 1, 1, 128), 1), ((1, 2, 1, 520, 64), 129),
+    # windows of many tiles: the key tiles run in rotated order
+    ((1, 4, 2, 4096, 128), 1024), ((1, 2, 1, 2000, 64), 700),
 ]
 
 
