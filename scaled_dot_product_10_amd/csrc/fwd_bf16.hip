@@ -205,13 +205,18 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     constexpr int KS = D / 16;  // k-steps of the Q.K^T product
     constexpr int DB = D / 32;  // 32-row blocks of O^T
     constexpr int ROWB = T::CPR * 16;  // bytes per tile row
-    __shared__ __attribute__((aligned(1024))) char smem[(SPLIT ? 8 : 4) * T::BYTES];
-    // BLOCK: listed key tiles (bits 0-23 tile, bit 24 + j: query block j may see it)
-    __shared__ uint32_t blist[BLOCK ? kMaxMaskTiles + 2 : 1];
-    __shared__ int bcount[BLOCK ? NW : 1];
-    // K buffers at [0, 2*BYTES), V buffers at [2*BYTES, 4*BYTES) (SPLIT: one
-    // such set per wave group)
-    const int gofs = SPLIT ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 8) * 4 * T::BYTES : 0;
+    // SPLIT and BLOCK: each wave group streams its own key tiles
+    constexpr bool GBUF = SPLIT || BLOCK;
+    __shared__ __attribute__((aligned(1024))) char smem[(GBUF ? 8 : 4) * T::BYTES];
+    // BLOCK: one list of key tiles per wave group, the tiles that one of its
+    // two query blocks may see (bits 0-23 tile, bit 24 + j: query block j of
+    // the workgroup may see it)
+    constexpr int LSTRIDE = kMaxMaskTiles + 2;
+    __shared__ uint32_t blist[BLOCK ? 2 * LSTRIDE : 1];
+    __shared__ int bcount[BLOCK ? 2 * NW : 1];
+    // K buffers at [0, 2*BYTES), V buffers at [2*BYTES, 4*BYTES) (SPLIT and
+    // BLOCK: one such set per wave group)
+    const int gofs = GBUF ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 8) * 4 * T::BYTES : 0;
     auto Kbuf = [&](int i) __attribute__((always_inline)) { return smem + gofs + (i & 1) * T::BYTES; };
     auto Vbuf = [&](int i) __attribute__((always_inline)) { return smem + gofs + (2 + (i & 1)) * T::BYTES; };
 
@@ -283,12 +288,15 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     const int lrot = LOCAL ? (lcnt - nbeg % lcnt) % lcnt : 0;
 
     if (BLOCK) {
-        // list the tiles below nend that a query block of this workgroup may
-        // see, in order: flags per thread, then a ballot/popcount compaction
+        // For each wave group, list the tiles below nend that one of its two
+        // query blocks may see, in order: flags per thread, then a ballot /
+        // popcount compaction per list.  Both groups then run max(count)
+        // positions; the shorter list is padded with entries that name no
+        // tile (never valid) and no query block.
         const int qb0 = m0 / kMaskBlock;
         const int nqb = min(BM / kMaskBlock, (S - m0 + kMaskBlock - 1) / kMaskBlock);
         const uint8_t* mrow = p.bmask + (int64_t)b * p.bm_sb + (int64_t)h * p.bm_sh + (int64_t)qb0 * p.nkb;
-        int base = 0;
+        int base[2] = {0, 0};
         for (int t0 = 0; t0 < nend; t0 += NT) {
             const int t = t0 + tid;
             uint32_t bits = 0;
@@ -297,24 +305,33 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
                 for (int j = 0; j < BM / kMaskBlock; ++j)
                     if (j < nqb && mrow[(int64_t)j * p.nkb + t]) bits |= 1u << j;
             }
-            const uint64_t bal = __builtin_amdgcn_ballot_w64(bits != 0);
-            const int within = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            if (lane == 0) bcount[wave] = __builtin_popcountll(bal);
-            __syncthreads();
-            int before = 0, total = 0;
+            int within[2];
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const int cw = bcount[w];
-                before += w < wave ? cw : 0;
-                total += cw;
+            for (int gl = 0; gl < 2; ++gl) {
+                const uint64_t bal = __builtin_amdgcn_ballot_w64(((bits >> (2 * gl)) & 3u) != 0);
+                within[gl] = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                if (lane == 0) bcount[gl * NW + wave] = __builtin_popcountll(bal);
             }
-            if (bits) blist[base + before + within] = (uint32_t)t | (bits << 24);
-            base += total;
+            __syncthreads();
+#pragma unroll
+            for (int gl = 0; gl < 2; ++gl) {
+                int before = 0, total = 0;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const int cw = bcount[gl * NW + w];
+                    before += w < wave ? cw : 0;
+                    total += cw;
+                }
+                if ((bits >> (2 * gl)) & 3u) blist[gl * LSTRIDE + base[gl] + before + within[gl]] = (uint32_t)t | (bits << 24);
+                base[gl] += total;
+            }
             __syncthreads();
         }
-        if (tid < 2) blist[base + tid] = 0;  // the two positions after the last: tile 0, no block
+        nend = max(base[0], base[1]);
+#pragma unroll
+        for (int gl = 0; gl < 2; ++gl)
+            for (int i = base[gl] + tid; i < nend + 2; i += NT) blist[gl * LSTRIDE + i] = 0xffffffu;
         __syncthreads();
-        nend = base;
         if (nend == 0) {  // no key visible to any query of this workgroup
             if (qi < S) {
                 uint16_t* orow = p.out + (row0 + qi) * D;
@@ -338,19 +355,20 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
             i -= i >= lcnt ? lcnt : 0;
             return (uint32_t)(nbeg + i);
         }
-        return BLOCK ? __builtin_amdgcn_readfirstlane(blist[n]) : (uint32_t)(n + toff);
+        return BLOCK ? __builtin_amdgcn_readfirstlane(blist[grp * LSTRIDE + n]) : (uint32_t)(n + toff);
     };
     auto tile_of = [&](uint32_t e) __attribute__((always_inline)) { return BLOCK ? (int)(e & 0xffffffu) : (int)e; };
-    // SPLIT: the position names a tile of the workgroup
-    auto valid = [&](uint32_t e) __attribute__((always_inline)) { return !SPLIT || (int)e < nall; };
+    // SPLIT, BLOCK: the position names a tile of the workgroup (BLOCK's
+    // padding entries name none)
+    auto valid = [&](uint32_t e) __attribute__((always_inline)) { return !GBUF || tile_of(e) < nall; };
     auto wave_sees = [&](uint32_t e) __attribute__((always_inline)) {
         return !BLOCK || ((e >> (24 + wave / 2)) & 1u) != 0;
     };
 
     // ---- prologue: K(nbeg), V(nbeg), K(nbeg+1) in flight while Q is loaded --
-    const int dw = SPLIT ? (wave & 3) : wave;  // wave's share of its group's tile loads
-    DmaPlan<D, false, SPLIT ? NW / 2 : NW> kdma;
-    DmaPlan<D, true, SPLIT ? NW / 2 : NW> vdma;
+    const int dw = GBUF ? (wave & 3) : wave;  // wave's share of its group's tile loads
+    DmaPlan<D, false, GBUF ? NW / 2 : NW> kdma;
+    DmaPlan<D, true, GBUF ? NW / 2 : NW> vdma;
     kdma.init(dw, lane);
     vdma.init(dw, lane);
     if (valid(ent(nbeg))) {
@@ -538,6 +556,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
             if (LOCAL && active(e1) && in_window(e1)) qk(Kbuf(n + 1));
             return;
         }
+        // BLOCK: a listed tile this wave's block may not see has P = 0 (set in
+        // the V phase); the phase runs only for the next tile's S product
+        if (BLOCK && !wave_sees(e0) && !(active(e1) && wave_sees(e1))) return;
         constexpr int NQK = 2 * KS, NPV = 4 * DB, NP = NQK + NPV, AHEAD = 4;
         const char* Kt = Kbuf(n + 1);
         const char* Vt = Vbuf(n);
@@ -568,9 +589,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
         __builtin_amdgcn_s_setprio(0);
     };
     // V(n): softmax of tile n (from S(n) of the previous M phase)
-    // BLOCK: a listed tile this wave's block may not see gets P = 0 (the
-    // matrix phase runs as usual: the workgroup's phases take as long as
-    // their busiest wave anyway)
+    // BLOCK: a listed tile this wave's block may not see gets P = 0
     auto vphase = [&](uint32_t e0) __attribute__((always_inline)) {
         if (active(e0) && in_window(e0)) {
             if (wave_sees(e0)) {
