@@ -2,16 +2,27 @@
 //
 // Same method as the bfloat16 kernel (key/value tiles through LDS, online
 // softmax, nothing of size S x S in device memory) on plain float32 vector
-// ALU arithmetic: one lane per query, 64 queries per workgroup, 16 keys per
-// step.  This is the path for float32 inputs, where the bfloat16 matrix
-// cores do not apply; it is a correctness path, not a throughput one.
+// ALU arithmetic.  This is the path for float32 inputs, where the bfloat16
+// matrix cores do not apply; it is a correctness path, sized for short
+// sequences, where the time is latency rather than arithmetic.
+//
+// Layout: a workgroup of eight waves owns QW queries (64 at D = 64, 32 at
+// D = 128).  Each lane holds 64 of its query's d's in registers, of q and of
+// the output accumulator (at D = 128 the two halves of a wave hold the two
+// halves of d and add their partial dot products with one lane swap).  The
+// eight waves (two per SIMD) split the key range: wave w takes the 16-key
+// steps n = w, w + 8, ..., each through its own K/V buffers in LDS (read as
+// 16-byte broadcasts), with the next step's tile loaded into registers while
+// the current one is used, so the loop has no workgroup barrier.  At the end
+// waves 1-7 hand (m, l, o) to wave 0 through LDS (over the K/V buffers),
+// which merges the eight partial softmaxes.
 #include "common.h"
 #include "launch.h"
 
 namespace attn {
 namespace {
 
-constexpr int BMF = 64;  // queries per workgroup (one wave)
+constexpr int NWF = 8;   // waves per workgroup (split of the key range)
 constexpr int BNF = 16;  // keys per step
 
 struct Params {
@@ -24,13 +35,27 @@ struct Params {
     float c;  // scale * log2(e), > 0
 };
 
+template <int D>
+struct F32Shape {
+    static constexpr int DS = D / 64;   // lanes per query
+    static constexpr int QW = 64 / DS;  // queries per workgroup
+    static constexpr int DL = D / DS;   // d's per lane (64)
+    static constexpr int TF = BNF * D;  // floats of one K or V step tile
+    static constexpr int LPT = TF / 64 / 4;  // 16-byte loads per lane per tile
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(BMF) void fwd_f32_kernel(Params p) {
-    __shared__ float Qs[BMF][D + 1];  // +1: lanes read different rows of one column
-    __shared__ float Ks[BNF][D];
-    __shared__ float Vs[BNF][D];
+__global__ __launch_bounds__(64 * NWF) void fwd_f32_kernel(Params p) {
+    using F = F32Shape<D>;
+    constexpr int DS = F::DS, QW = F::QW, DL = F::DL, TF = F::TF, LPT = F::LPT;
+    // per wave: K, V of its step; after the loop: o, m, l of waves 1..NWF-1
+    constexpr int KVF = NWF * 2 * TF, REDF = (NWF - 1) * (DL + 2) * 64;
+    __shared__ __attribute__((aligned(16))) float lds[KVF > REDF ? KVF : REDF];
 
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    auto red = [&](int w, int i) __attribute__((always_inline)) -> float& { return lds[(w * (DL + 2) + i) * 64 + lane]; };
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bh = blockIdx.x / p.nq;
     int tile = blockIdx.x % p.nq;
     if (CAUSAL) tile = p.nq - 1 - tile;
@@ -38,75 +63,157 @@ __global__ __launch_bounds__(BMF) void fwd_f32_kernel(Params p) {
     const int h = bh % p.Hq;
     const int kvh = h / p.group;
     const int S = p.S;
-    const int m0 = tile * BMF;
-    const int qi = m0 + tid;
+    const int m0 = tile * QW;
+    const int qi = m0 + lane % QW;      // this lane's query
+    const int d0 = (lane / QW) * DL;    // its first d
     const int64_t row0 = (int64_t)bh * S;
     const int64_t kvrow0 = ((int64_t)b * p.Hkv + kvh) * S;
 
-    for (int idx = tid; idx < BMF * D; idx += BMF) {
-        const int r = idx / D, d = idx % D;
-        Qs[r][d] = (m0 + r < S) ? p.q[(row0 + m0 + r) * D + d] : 0.f;
-    }
-
-    float o[D];
+    // q: rows past the end repeat row S - 1 (their results are never stored)
+    float q[DL];
+    {
+        const float* qp = p.q + (row0 + min(qi, S - 1)) * D + d0;
 #pragma unroll
-    for (int d = 0; d < D; ++d) o[d] = 0.f;
+        for (int d = 0; d < DL; d += 4) {
+            const f32x4 x = *(const f32x4*)(qp + d);
+            q[d] = x[0];
+            q[d + 1] = x[1];
+            q[d + 2] = x[2];
+            q[d + 3] = x[3];
+        }
+    }
+    float o[DL];
+#pragma unroll
+    for (int d = 0; d < DL; ++d) o[d] = 0.f;
     float m = -INFINITY, l = 0.f;
     const float c = p.c;
 
-    const int qlast = min(m0 + BMF, S) - 1;
+    const int qlast = min(m0 + QW, S) - 1;
     const int ntiles = (S + BNF - 1) / BNF;
     const int nend = CAUSAL ? min(ntiles, qlast / BNF + 1) : ntiles;
 
-    for (int n = 0; n < nend; ++n) {
+    // Step tile n of K and V into registers: lane t's 16-byte load i covers
+    // floats (i * 64 + t) * 4 .. +3 of the tile (rows past S read as zero)
+    f32x4 kr[LPT], vr[LPT];
+    auto load = [&](int n) __attribute__((always_inline)) {
         const int n0 = n * BNF;
-        __syncthreads();  // previous tile consumed (and Qs written, first time)
-        for (int idx = tid; idx < BNF * D; idx += BMF) {
-            const int r = idx / D, d = idx % D;
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int f = (i * 64 + lane) * 4;
+            const int r = f / D;
             const bool ok = n0 + r < S;
-            Ks[r][d] = ok ? p.k[(kvrow0 + n0 + r) * D + d] : 0.f;
-            Vs[r][d] = ok ? p.v[(kvrow0 + n0 + r) * D + d] : 0.f;
+            const int64_t off = (kvrow0 + n0 + (ok ? r : 0)) * D + f % D;
+            kr[i] = ok ? *(const f32x4*)(p.k + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+            vr[i] = ok ? *(const f32x4*)(p.v + off) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        __syncthreads();
+    };
+    float* Ks = lds + wave * 2 * TF;
+    float* Vs = Ks + TF;
+    if (wave < nend) load(wave);
+    for (int n = wave; n < nend; n += NWF) {
+        // this wave's buffers are free: its reads of the previous step are
+        // done (LDS operations of one wave complete in order)
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            *(f32x4*)(Ks + (i * 64 + lane) * 4) = kr[i];
+            *(f32x4*)(Vs + (i * 64 + lane) * 4) = vr[i];
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (n + NWF < nend) load(n + NWF);
+        const int n0 = n * BNF;
 
         float s[BNF];
         float mt = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < BNF; ++j) {
-            float dot = 0.f;
-#pragma unroll 16
-            for (int d = 0; d < D; ++d) dot = fmaf(Qs[tid][d], Ks[j][d], dot);
-            const int key = n0 + j;
-            s[j] = ((CAUSAL && key > qi) || key >= S) ? -INFINITY : dot;
-            mt = fmaxf(mt, s[j]);
+        for (int j0 = 0; j0 < BNF; j0 += 4) {  // four keys at a time: independent chains
+            float dot[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int d = 0; d < DL; d += 4) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const f32x4 kk = *(const f32x4*)(Ks + (j0 + u) * D + d0 + d);
+                    dot[u] = fmaf(q[d], kk[0], dot[u]);
+                    dot[u] = fmaf(q[d + 1], kk[1], dot[u]);
+                    dot[u] = fmaf(q[d + 2], kk[2], dot[u]);
+                    dot[u] = fmaf(q[d + 3], kk[3], dot[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float x = dot[u];
+                if (DS == 2) {  // the other half of d, held by lane (lane + 32) % 64
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+                    x = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                }
+                const int key = n0 + j0 + u;
+                s[j0 + u] = ((CAUSAL && key > qi) || key >= S) ? -INFINITY : x;
+                mt = fmaxf(mt, s[j0 + u]);
+            }
         }
         const float mnew = fmaxf(m, mt);
-        if (mnew == -INFINITY) continue;  // whole step masked for this lane
-        // (s - m) * c: exactly 0 for the largest score, so its weight is exactly 1
-        const float alpha = fast_exp2((m - mnew) * c);
-        float psum = 0.f;
+        if (mnew != -INFINITY) {  // else the whole step is masked for this lane
+            // (s - m) * c: exactly 0 for the largest score, so its weight is exactly 1
+            const float alpha = fast_exp2((m - mnew) * c);
+            float psum = 0.f;
 #pragma unroll
-        for (int j = 0; j < BNF; ++j) {
-            s[j] = fast_exp2((s[j] - mnew) * c);
-            psum += s[j];
+            for (int j = 0; j < BNF; ++j) {
+                s[j] = fast_exp2((s[j] - mnew) * c);
+                psum += s[j];
+            }
+            l = fmaf(l, alpha, psum);
+            m = mnew;
+#pragma unroll
+            for (int d = 0; d < DL; d += 4) {
+                float a0 = o[d] * alpha, a1 = o[d + 1] * alpha, a2 = o[d + 2] * alpha, a3 = o[d + 3] * alpha;
+#pragma unroll
+                for (int j = 0; j < BNF; ++j) {
+                    const f32x4 vv = *(const f32x4*)(Vs + j * D + d0 + d);
+                    a0 = fmaf(s[j], vv[0], a0);
+                    a1 = fmaf(s[j], vv[1], a1);
+                    a2 = fmaf(s[j], vv[2], a2);
+                    a3 = fmaf(s[j], vv[3], a3);
+                }
+                o[d] = a0;
+                o[d + 1] = a1;
+                o[d + 2] = a2;
+                o[d + 3] = a3;
+            }
         }
-        l = fmaf(l, alpha, psum);
-        m = mnew;
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            float acc = o[d] * alpha;
-#pragma unroll
-            for (int j = 0; j < BNF; ++j) acc = fmaf(s[j], Vs[j][d], acc);
-            o[d] = acc;
-        }
+        __builtin_amdgcn_wave_barrier();
     }
 
+    // merge: o = sum_w o_w 2^((m_w - M) c), l likewise, M = max_w m_w (a
+    // wave that saw no key of this query has m_w = -inf and weight 0)
+    __syncthreads();  // every wave is done with its K/V buffers
+    if (wave > 0) {
+#pragma unroll
+        for (int d = 0; d < DL; ++d) red(wave - 1, d) = o[d];
+        red(wave - 1, DL) = m;
+        red(wave - 1, DL + 1) = l;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    float mm = m;
+#pragma unroll
+    for (int w = 0; w < NWF - 1; ++w) mm = fmaxf(mm, red(w, DL));
+    const float a = m == -INFINITY ? 0.f : fast_exp2((m - mm) * c);
+    l *= a;
+#pragma unroll
+    for (int d = 0; d < DL; ++d) o[d] *= a;
+#pragma unroll
+    for (int w = 0; w < NWF - 1; ++w) {
+        const float mw = red(w, DL);
+        const float aw = mw == -INFINITY ? 0.f : fast_exp2((mw - mm) * c);
+        l = fmaf(red(w, DL + 1), aw, l);
+#pragma unroll
+        for (int d = 0; d < DL; ++d) o[d] = fmaf(red(w, d), aw, o[d]);
+    }
     if (qi < S) {
         const float inv = 1.0f / l;
-        float* orow = p.out + (row0 + qi) * D;
+        float* orow = p.out + (row0 + qi) * D + d0;
 #pragma unroll
-        for (int d = 0; d < D; d += 4) *(f32x4*)(orow + d) = f32x4{o[d], o[d + 1], o[d + 2], o[d + 3]} * inv;
-        if (p.lse) p.lse[row0 + qi] = (m * c + __log2f(l)) * kLn2;
+        for (int d = 0; d < DL; d += 4) *(f32x4*)(orow + d) = f32x4{o[d], o[d + 1], o[d + 2], o[d + 3]} * inv;
+        if (p.lse && d0 == 0) p.lse[row0 + qi] = (mm * c + __log2f(l)) * kLn2;
     }
 }
 
@@ -114,7 +221,7 @@ template <int D, bool CAUSAL>
 hipError_t launch(const Params& prm, int blocks, hipStream_t stream) {
     Params arg = prm;
     void* args[] = {&arg};
-    return hipLaunchKernel((const void*)&fwd_f32_kernel<D, CAUSAL>, dim3(blocks), dim3(BMF), args, 0, stream);
+    return hipLaunchKernel((const void*)&fwd_f32_kernel<D, CAUSAL>, dim3(blocks), dim3(64 * NWF), args, 0, stream);
 }
 
 }  // namespace
@@ -130,7 +237,8 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
     prm.Hkv = a.Hkv;
     prm.S = a.S;
     prm.group = a.Hq / a.Hkv;
-    prm.nq = (a.S + BMF - 1) / BMF;
+    const int qw = a.D == 128 ? F32Shape<128>::QW : F32Shape<64>::QW;
+    prm.nq = (a.S + qw - 1) / qw;
     prm.c = a.scale * kLog2e;
     const int blocks = (int)((int64_t)a.B * a.Hq * prm.nq);
     if (a.D == 128) return a.causal ? launch<128, true>(prm, blocks, stream) : launch<128, false>(prm, blocks, stream);
