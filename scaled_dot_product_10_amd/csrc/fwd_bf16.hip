@@ -714,6 +714,7 @@ struct PersistParams {
     int Hq, Hkv, S, group, nq;
     int units;   // units per head (causal nq / 2, full nq)
     int rounds;  // units per workgroup
+    int hpr;     // causal, > 0: heads per item round (see item_bh_tile); 0: pairs of one head
     float c;     // scale * log2(e), > 0
     uint64_t* stamps;
 };
@@ -766,8 +767,19 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
 
     // item i of this workgroup -> (b * Hq + h, query tile); key tiles it runs
     auto item_bh_tile = [&](int i, int& bh, int& tile) __attribute__((always_inline)) {
-        const int r = CAUSAL ? i >> 1 : i;
         const uint32_t w = blockIdx.x | (uint32_t)opaque_szero();
+        if (CAUSAL && p.hpr > 0) {
+            // item round i of XCD x: its G/8 workgroups take all nq tiles of
+            // hpr heads, workgroup c tile j = c % nq in even rounds and
+            // nq-1-j in odd ones (descending), so each head has one read
+            // front and every workgroup the same 4 (nq + 1) key tiles per
+            // two rounds
+            const int nq = p.nq, c = (int)(w / 8u), j = c % nq;
+            bh = ((int)(w % 8u) * p.rounds * 2 + i) * p.hpr + c / nq;
+            tile = (i & 1) ? nq - 1 - j : j;
+            return;
+        }
+        const int r = CAUSAL ? i >> 1 : i;
         const uint32_t L = ((w % 8u) * (uint32_t)p.rounds + (uint32_t)r) * (G / 8u) + w / 8u;
         bh = (int)(L / (uint32_t)p.units);
         const int j = (int)(L % (uint32_t)p.units);
@@ -1276,6 +1288,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
             pp.nq = prm.nq;
             pp.units = a.causal ? prm.nq / 2 : prm.nq;
             pp.rounds = (int)(units / cus);
+            // causal: item rounds of whole heads when an XCD's workgroups
+            // hold the tiles of whole heads
+            pp.hpr = a.causal && (cus / 8) % prm.nq == 0 ? cus / 8 / prm.nq : 0;
             pp.c = prm.c;
             pp.stamps = prm.stamps;
             if (a.D == 128)
