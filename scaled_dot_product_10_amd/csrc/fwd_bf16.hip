@@ -698,13 +698,19 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
 // registers at that item's last softmax phase).  The previous item's output
 // is normalised and stored during the next item's first softmax phase.
 //
-// Items: each head's query tiles form units; causal: unit j = tiles nq-1-j
-// and j (a long and a short item with 4 (nq + 1) key tiles together, so every
-// unit is equally long; the short one runs its key tiles in descending
-// order); full: unit j = tile j.  Workgroup w runs unit r G + (w % 8) G/8 +
-// w / 8 in round r: workgroups on one XCD (the hardware deals them
-// round-robin over the 8 XCDs) take consecutive units, i.e. the tiles of a
-// few heads, whose key/value tiles they read in step through the XCD's L2.
+// Items (R = rounds, G workgroups; the hardware deals workgroups round-robin
+// over the 8 XCDs, so workgroup w runs on XCD w % 8):
+// - causal, with (G/8) % nq == 0: item i of workgroup w = 8c + x is tile
+//   j = c % nq (i even) or nq-1-j (i odd, key tiles in descending order) of
+//   head (2R x + i) hpr + c / nq, hpr = (G/8) / nq.  Every workgroup runs
+//   4 (nq + 1) key tiles per two items, and in each item round an XCD holds
+//   all tiles of hpr heads: a head's items start together (ascending) or end
+//   together (descending), so each head has one read front and its
+//   key/value tiles are read once, in step, through the XCD's L2.
+// - causal otherwise: unit j of a head = its tiles nq-1-j and j (the second
+//   in descending order); full attention: unit j = tile j.  Workgroup w runs
+//   unit (x R + r) G/8 + c in round r: an XCD's workgroups take consecutive
+//   units, the tiles of a few heads.
 struct PersistParams {
     const uint16_t* q;
     const uint16_t* k;

@@ -252,8 +252,12 @@ def test_stamped_launch(name, causal):
 # query tiles back to back, the key/value stream continuing across them):
 # shapes whose unit count is a multiple of the 256 compute units, ragged S,
 # D 64 and 128, GQA, one and several rounds; every element compared.
+# causal ones with nq dividing the 32 compute units of an XCD take item rounds
+# of whole heads; (1, 256, 32, 1500, 64) has nq = 6 and takes pairs of one
+# head's tiles per round
 PERSIST = [
     (1, 64, 8, 2000, 64, True), (2, 64, 16, 1000, 128, True), (4, 64, 16, 1000, 128, True),
+    (1, 256, 32, 1500, 64, True),
     (1, 32, 4, 2000, 128, False), (2, 128, 32, 300, 64, False), (1, 256, 256, 256, 128, False),
 ]
 
