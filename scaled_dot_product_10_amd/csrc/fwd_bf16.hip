@@ -721,6 +721,7 @@ struct PersistParams {
     int units;   // units per head (causal nq / 2, full nq)
     int rounds;  // units per workgroup
     int hpr;     // causal, > 0: heads per item round (see item_bh_tile); 0: pairs of one head
+    int window;  // sliding window (LOCAL): keys q - window + 1 .. q
     float c;     // scale * log2(e), > 0
     uint64_t* stamps;
 };
@@ -743,8 +744,9 @@ __device__ __forceinline__ int opaque_szero() {
     return z;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool LOCAL = false>
 __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
+    static_assert(!LOCAL || CAUSAL, "a sliding window is a causal mask");
     using T = Tile<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
@@ -766,7 +768,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     const int g = lane >> 5;
     char* const qst = smem + 4 * T::BYTES + wave * QWB;  // this wave's Q rows (K-tile layout)
     const int S = p.S;
-    const int nitems = p.rounds * (CAUSAL ? 2 : 1);
+    const int nitems = p.rounds * (CAUSAL && !LOCAL ? 2 : 1);
     const uint32_t G = gridDim.x;
     // XCD x (blockIdx % 8) runs units [x U/8, (x+1) U/8) of all U = rounds G:
     // consecutive heads, G/8 units per round
@@ -774,6 +776,16 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     // item i of this workgroup -> (b * Hq + h, query tile); key tiles it runs
     auto item_bh_tile = [&](int i, int& bh, int& tile) __attribute__((always_inline)) {
         const uint32_t w = blockIdx.x | (uint32_t)opaque_szero();
+        if (LOCAL) {
+            // item round i of XCD x: all nq tiles of hpr heads, workgroup c
+            // tile (c + i nq / R) % nq: over its R items a workgroup meets
+            // tiles spread over the sequence, so the short first tiles (whose
+            // windows are cut by the sequence start) fall to different ones
+            const int nq = p.nq, c = (int)(w / 8u);
+            bh = ((int)(w % 8u) * p.rounds + i) * p.hpr + c / nq;
+            tile = (c % nq + i * nq / p.rounds) % nq;
+            return;
+        }
         if (CAUSAL && p.hpr > 0) {
             // item round i of XCD x: its G/8 workgroups take all nq tiles of
             // hpr heads, workgroup c tile j = c % nq in even rounds and
@@ -795,6 +807,14 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
         const int Sx = S | opaque_szero(), nt = (Sx + BN - 1) / BN;
         return CAUSAL ? min(nt, (min(tile * BM + BM, Sx) - 1) / BN + 1) : nt;
     };
+    // LOCAL: an item's key tiles lbeg .. lend-1 (the window of its first
+    // query to its diagonal), run in rotated order from tile lbeg + rot, the
+    // one congruent to 0 modulo their count: the workgroups of a head that
+    // start an item round together then read the same tile at the same time
+    auto local_beg = [&](int tile_) __attribute__((always_inline)) {
+        return max(0, tile_ * BM - (p.window | opaque_szero()) + 1) / BN;
+    };
+    auto local_first = [&](int beg, int cnt) __attribute__((always_inline)) { return beg + (cnt - beg % cnt) % cnt; };
     // The stream position: position k of the current item (nk key tiles,
     // head bh, query tile), at key tile kt, moving by dk; the next item's
     // head, query tile, key tile count and direction.  Every item has at
@@ -806,6 +826,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     // head's workgroups read at most two key tiles at a time (the ascending
     // and the descending front) and the XCD's L2 serves the other reads.
     int it = 0, k = 0, nk, bh, tile, kt = 0, dk = 1;  // the next item's direction: CAUSAL ? -dk : dk
+    int lbeg = 0, lend = 0;  // LOCAL: the current item's key tiles
     int nbh = 0, ntile = 0;
     auto kv_of = [&](int bh_) __attribute__((always_inline)) {
         const int b = bh_ / p.Hq, h = bh_ % p.Hq;
@@ -813,6 +834,12 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     };
     item_bh_tile(0, bh, tile);
     nk = item_tiles(tile);
+    if (LOCAL) {
+        lbeg = local_beg(tile);
+        lend = nk;
+        nk = lend - lbeg;
+        kt = local_first(lbeg, nk);
+    }
     bool has_next = nitems > 1;
     if (has_next) item_bh_tile(1, nbh, ntile);
     // DMA sources: K of position n+2 and V of position n+1 (tile pointers
@@ -825,22 +852,31 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     // element offset of the next item's first key tile (the last one when it
     // runs in descending order)
     auto first_tile = [&]() __attribute__((always_inline)) {
+        if (LOCAL) return kv_of(nbh);  // LOCAL: the next item's head; tiles are placed by index
         return kv_of(nbh) + (CAUSAL && dk > 0 ? (int64_t)(item_tiles(ntile) - 1) * TSTEP : 0);
     };
     int64_t knext = has_next ? first_tile() : 0;
     const char* kp = (const char*)(p.k + kv0 + 2 * TSTEP);
     const char* vp = (const char*)(p.v + kv0 + TSTEP);
+    int64_t kvcur = kv0;  // LOCAL: the current item's head (element offset of key 0)
     auto advance_item = [&]() __attribute__((always_inline)) {
         ++it;
         bh = nbh;
         tile = ntile;
         nk = item_tiles(tile);
-        if (CAUSAL) {
+        if (CAUSAL && !LOCAL) {
             dk = -dk;
             cstep = -cstep;
         }
         k = 0;
         kt = dk < 0 ? nk - 1 : 0;
+        if (LOCAL) {
+            lbeg = local_beg(tile);
+            lend = nk;
+            nk = lend - lbeg;
+            kt = local_first(lbeg, nk);
+            kvcur = knext;
+        }
         has_next = it + 1 < nitems;
         if (has_next) {
             item_bh_tile(it + 1, nbh, ntile);
@@ -893,9 +929,13 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
 
     // ---- prologue: Q of the first item, K(0), V(0), K(1) ---------------------
     q_dma(bh, tile);
-    kdma.issue(p.k + kv0, 0, S, Kbuf(0), wave);
-    vdma.issue(p.v + kv0, 0, S, Vbuf(0), wave);
-    kdma.issue(p.k + kv0, BN, S, Kbuf(1), wave);  // the item has 4 or more key tiles
+    {
+        // LOCAL: the first two tiles of the rotated order
+        const int t0 = LOCAL ? kt : 0, t1 = LOCAL ? (kt + 1 < lend ? kt + 1 : lbeg) : 1;
+        kdma.issue(p.k + kv0, t0 * BN, S, Kbuf(0), wave);
+        vdma.issue(p.v + kv0, t0 * BN, S, Vbuf(0), wave);
+        kdma.issue(p.k + kv0, t1 * BN, S, Kbuf(1), wave);  // the item has 4 or more key tiles
+    }
     phase_barrier(true);
     q_read();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -979,13 +1019,16 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
             // kofs = 32 sb + 8 (r / 4) + r % 4; it is masked when kofs > hi.
             // The sign of hi - kofs selects -inf bit by bit (v_bfi), so no
             // lane masks are held in scalar registers.
+            // LOCAL: also masked when kofs <= lo (key before the row's window)
             const int hi = (CAUSAL ? min(qi, S - 1) : S - 1) - (n0 + g * 4);
+            const int lo = LOCAL ? qi - p.window - (n0 + g * 4) : 0;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kofs = sb * 32 + (r >> 2) * 8 + (r & 3);
-                    const uint32_t m = (uint32_t)((hi - kofs) >> 31);  // all ones when masked
+                    uint32_t m = (uint32_t)((hi - kofs) >> 31);  // all ones when masked
+                    if (LOCAL) m |= (uint32_t)((kofs - lo - 1) >> 31);
                     sacc[sb][r] = __uint_as_float((__float_as_uint(sacc[sb][r]) & ~m) | (0xff800000u & m));
                 }
             }
@@ -1028,14 +1071,23 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     // descending item's first tile already gives every row a finite max.
     // ncommon: number of positions k with 2 <= k < nk - 3 (the DMA's common
     // case: whole tiles in this item)
-    int kact, kmask, ncommon;
+    // LOCAL: kwin, the first key tile holding a key of this wave's windows,
+    // and kwfull, the first tile inside every row's window.
+    int kact, kmask, ncommon, kwin = 0, kwfull = 0;
     auto set_limits = [&]() __attribute__((always_inline)) {
         kact = CAUSAL ? (qwmin + 31) / BN : nk - 1;
         const int Sx = S | opaque_szero();
         const int ktail = Sx / BN;  // the partial last key tile, or one past the last
         kmask = CAUSAL ? min((qwmin + 1) / BN, ktail) : ktail;
         ncommon = max(nk - 5, 0);
+        if (LOCAL) {
+            const int W = p.window | opaque_szero();
+            kwin = max(qwmin - W + 1, 0) / BN;
+            kwfull = (max(qwmin + 31 - W + 1, 0) + BN - 1) / BN;
+        }
     };
+    // LOCAL: this wave sees key tile t (it holds a key of one of its windows)
+    auto sees = [&](int t) __attribute__((always_inline)) { return (unsigned)(t - kwin) <= (unsigned)(kact - kwin); };
     set_limits();
     // V phase of position (it, k).  The rare events are tested with one range
     // check: at an item's first tile (k = 0) the previous item's output goes
@@ -1061,8 +1113,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
                 q_read();
             }
         }
-        if (!CAUSAL || kt <= kact) {
-            softmax(kt * BN, kt >= kmask);
+        if (LOCAL ? sees(kt) : (!CAUSAL || kt <= kact)) {
+            softmax(kt * BN, kt >= kmask || (LOCAL && kt < kwfull));
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) pb[i] = bf16x8{};  // see the M phase
@@ -1079,10 +1131,37 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     const int qdma_k = grp;
     const uint32_t lbase = lds_addr(smem);
     uint32_t kb_off = 0;  // (n & 1) * tile bytes
+    // LOCAL: key tile of position k + d (d = 1, 2) of the current item, or of
+    // the next item's position k + d - nk, and its head
+    auto local_pos = [&](int d, int& t, int64_t& hb) __attribute__((always_inline)) {
+        if (k + d < nk) {
+            t = kt + d;
+            if (t >= lend) t -= nk;
+            hb = kvcur;
+        } else {
+            const int nb = local_beg(ntile), nn = item_tiles(ntile) - nb;
+            t = local_first(nb, nn) + (k + d - nk);
+            if (t >= nb + nn) t -= nn;
+            hb = knext;
+        }
+    };
     auto dma = [&]() __attribute__((always_inline)) {
         const uint32_t lk = lbase + kb_off;
         const uint32_t lv = lbase + 2u * T::BYTES + (kb_off ^ (uint32_t)T::BYTES);
-        if ((unsigned)(k - 2) < (unsigned)ncommon) {
+        if (LOCAL) {
+            // whole tiles (the sequence is a whole number of query tiles)
+            int t;
+            int64_t hb;
+            if (k + 2 < nk || has_next) {
+                local_pos(2, t, hb);
+                kdma.issue_at(p.k + hb + (int64_t)t * TSTEP, true, 0, lk, wave);
+            }
+            if (k + 1 < nk || has_next) {
+                local_pos(1, t, hb);
+                vdma.issue_at(p.v + hb + (int64_t)t * TSTEP, true, 0, lv, wave);
+            }
+            if (k == qdma_k && has_next) q_dma(nbh, ntile);
+        } else if ((unsigned)(k - 2) < (unsigned)ncommon) {
             kdma.issue_at((const uint16_t*)kp, true, 0, lk, wave);
             vdma.issue_at((const uint16_t*)vp, true, 0, lv, wave);
             kp += cstep;
@@ -1116,9 +1195,15 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     // product nobody uses (a tile the wave does not see, or after the last
     // position, on the stale but in-bounds other buffer) is harmless.
     auto mphase = [&]() __attribute__((always_inline)) {
-        // descending items also need the M phase of the position before the
-        // first tile the wave sees (kact + 1), for that tile's S product
-        if (CAUSAL && kt > kact - (dk >> 1) && !(k == nk - 1 && has_next)) return;
+        if (LOCAL) {
+            // the rotated order puts tiles this wave does not see anywhere:
+            // the phase runs for this tile, or for the next one's S product
+            if (!sees(kt) && !(k + 1 < nk ? sees(kt + 1 < lend ? kt + 1 : lbeg) : has_next)) return;
+        } else if (CAUSAL && kt > kact - (dk >> 1) && !(k == nk - 1 && has_next)) {
+            // descending items also need the M phase of the position before
+            // the first tile the wave sees (kact + 1), for that tile's S product
+            return;
+        }
         __builtin_amdgcn_s_setprio(1);
         {
             constexpr int NQK = 2 * KS, NPV = 4 * DB, NP = NQK + NPV, AHEAD = 4;
@@ -1154,6 +1239,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     auto advance = [&]() __attribute__((always_inline)) {
         np ^= 1;
         kt += dk;
+        if (LOCAL && kt == lend) kt = lbeg;
         if (++k < nk) return true;
         if (!has_next) return false;
         advance_item();
@@ -1192,11 +1278,12 @@ __global__ __launch_bounds__(NT) void fwd_bf16_persist_kernel(PersistParams p) {
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool LOCAL = false>
 hipError_t launch_persist(const PersistParams& prm, uint32_t grid, hipStream_t stream) {
     PersistParams arg = prm;
     void* args[] = {&arg};
-    return hipLaunchKernel((const void*)&fwd_bf16_persist_kernel<D, CAUSAL>, dim3(grid), dim3(NT), args, 0, stream);
+    return hipLaunchKernel((const void*)&fwd_bf16_persist_kernel<D, CAUSAL, LOCAL>, dim3(grid), dim3(NT), args, 0,
+                           stream);
 }
 
 // Compute units of the stream's device (cached per device).
@@ -1272,8 +1359,36 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
         return a.causal ? launch<64, true, false, true>(prm, stream) : launch<64, false, false, true>(prm, stream);
     }
     // a window of at least S keys hides nothing the causal mask shows
-    if (a.causal && a.window > 0 && a.window < a.S)
+    if (windowed) {
+        // persistent form: whole query tiles (every item then has 4 or more
+        // key tiles), whole rounds of tiles, and the tiles of whole heads on
+        // each XCD's compute units
+        const int cus = device_cus(stream);
+        const int64_t units = (int64_t)a.B * a.Hq * prm.nq;
+        if (a.S % BM == 0 && cus >= 8 && cus % 8 == 0 && (cus / 8) % prm.nq == 0 && units % cus == 0 &&
+            units / cus <= (1 << 20)) {
+            PersistParams pp;
+            pp.q = prm.q;
+            pp.k = prm.k;
+            pp.v = prm.v;
+            pp.out = prm.out;
+            pp.lse = prm.lse;
+            pp.Hq = prm.Hq;
+            pp.Hkv = prm.Hkv;
+            pp.S = prm.S;
+            pp.group = prm.group;
+            pp.nq = prm.nq;
+            pp.units = prm.nq;
+            pp.rounds = (int)(units / cus);
+            pp.hpr = cus / 8 / prm.nq;
+            pp.window = a.window;
+            pp.c = prm.c;
+            pp.stamps = prm.stamps;
+            return a.D == 128 ? launch_persist<128, true, true>(pp, cus, stream)
+                              : launch_persist<64, true, true>(pp, cus, stream);
+        }
         return a.D == 128 ? launch<128, true, true>(prm, stream) : launch<64, true, true>(prm, stream);
+    }
     // Persistent form: plain attention, every item at least one 256-query
     // tile long (so each has 4 or more key tiles), causal query tiles in
     // pairs, and whole rounds of units over the compute units.
@@ -1297,6 +1412,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
             // causal: item rounds of whole heads when an XCD's workgroups
             // hold the tiles of whole heads
             pp.hpr = a.causal && (cus / 8) % prm.nq == 0 ? cus / 8 / prm.nq : 0;
+            pp.window = 0;
             pp.c = prm.c;
             pp.stamps = prm.stamps;
             if (a.D == 128)

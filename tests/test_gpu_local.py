@@ -47,6 +47,25 @@ def test_small_full_compare(orc, shape, window):
     G.check_close(f"local {shape} W={window}", G.host(out), ref_o, "bf16", G.host(lse), ref_l)
 
 
+# Whole query tiles, whole rounds of tiles over 256 compute units and whole
+# heads per XCD: these take the persistent window form (one workgroup per
+# compute unit over 1, 2 and 4 item rounds; the 4-round one has the short
+# first tiles of each head, whose windows the sequence start cuts).
+PERSIST = [((1, 32, 8, 2048, 128), 300), ((2, 64, 16, 1024, 64), 100), ((1, 64, 16, 4096, 128), 1024),
+           ((1, 64, 64, 4096, 64), 64)]
+
+
+@pytest.mark.parametrize("shape,window", PERSIST, ids=lambda c: str(c))
+def test_persistent_full_compare(orc, shape, window):
+    B, Hq, Hkv, S, D = shape
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", seed=3300 + S + window)
+    sc = 1.0 / math.sqrt(D)
+    out, lse = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=True, scale=sc, window=window)
+    torch.cuda.synchronize()
+    ref_o, ref_l = orc.attn_fwd_local(q.f32, k.f32, v.f32, sc, window)
+    G.check_close(f"local persistent {shape} W={window}", G.host(out), ref_o, "bf16", G.host(lse), ref_l)
+
+
 def test_wide_window_is_causal():
     q, k, v = inputs.make_qkv(1, 4, 2, 700, 128, "bf16", seed=3100)
     Q, K, V = G.dev(q), G.dev(k), G.dev(v)
