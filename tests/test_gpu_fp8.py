@@ -104,6 +104,30 @@ def test_moving_reference(orc, shape, step, causal):
     check_fp8(orc, f"fp8 ramp {step:+g} {shape} causal={causal}", q, k, v, causal, out, lse)
 
 
+# Causal grids of 256 to 768 workgroups (several per compute unit, the head
+# groups of the XCD schedule, ragged S, GQA); every element compared.
+GRIDS = [(1, 64, 8, 2000, 64), (2, 64, 16, 1000, 128), (1, 256, 32, 1500, 64)]
+
+
+@pytest.mark.parametrize("shape", GRIDS, ids=lambda s: "B{}H{}kv{}S{}D{}".format(*s))
+def test_grid_full_compare(orc, shape):
+    B, Hq, Hkv, S, D = shape
+    q, k, v = inputs.make_qkv_fp8(B, Hq, Hkv, S, D, seed=6400 + S + D)
+    out, lse = api.fwd_fp8(codes(q), codes(k), codes(v), q.scale, k.scale, v.scale, causal=True)
+    torch.cuda.synchronize()
+    check_fp8(orc, f"fp8 grid {shape}", q, k, v, True, out, lse)
+
+
+@pytest.mark.parametrize("step", [20.0, 70.0, -20.0], ids=lambda s: f"step{s:+g}")
+def test_grid_moving_reference(orc, step):
+    """The ramps of test_moving_reference over 512 workgroups."""
+    B, Hq, Hkv, S, D = 1, 128, 16, 1024, 128
+    q, k, v = inputs.make_qkv_fp8_ramp(B, Hq, Hkv, S, D, step, seed=6500 + int(step))
+    out, lse = api.fwd_fp8(codes(q), codes(k), codes(v), q.scale, k.scale, v.scale, causal=True)
+    torch.cuda.synchronize()
+    check_fp8(orc, f"fp8 grid ramp {step:+g}", q, k, v, True, out, lse)
+
+
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
 def test_long_sequence_sampled(orc, causal):
     """S = 32768: the weights' reference keeps moving over 512 key tiles."""
