@@ -247,7 +247,9 @@ __global__ __launch_bounds__(NT2) void bwd_dkdv_kernel(BwdParams p) {
                 sacc = mfma32x32x16(aq, bk, sacc);
                 dpacc = mfma32x32x16(ao, bv, dpacc);
             }
-            // row r of the accumulators: query qb + 8(r/4) + 4g + r%4
+            // row r of the accumulators: query qb + 8(r/4) + 4g + r%4, masked
+            // (causal) when its offset 8(r/4) + r%4 is below lo
+            const int lo = key - qb - 4 * g;
             f32x16 pv, dsv;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(NT2) void bwd_dkdv_kernel(BwdParams p) {
                 for (int e = 0; e < 4; ++e) {
                     const int r = q4 * 4 + e;
                     float pr = fast_exp2(fmaf(sacc[r], c, -l4[e]));
-                    if (CAUSAL && key > m0 + rl + e) pr = 0.f;
+                    if (CAUSAL && q4 * 8 + e < lo) pr = 0.f;
                     pv[r] = pr;
                     dsv[r] = pr * (dpacc[r] - d4[e]);
                 }
@@ -405,13 +407,14 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
                 sacc = mfma32x32x16(ak, qreg[ks], sacc);
                 dpacc = mfma32x32x16(av, oreg[ks], dpacc);
             }
-            // row r: key kb0 + 8(r/4) + 4g + r%4
+            // row r: key kb0 + 8(r/4) + 4g + r%4, masked when its offset
+            // 8(r/4) + r%4 passes hi (past this lane's query or past S)
+            const int hi = (CAUSAL ? min(qi, S - 1) : S - 1) - kb0 - 4 * g;
             f32x16 dsv;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int kj = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
                 float pr = fast_exp2(fmaf(sacc[r], c, -l2));
-                if (kj >= S || (CAUSAL && kj > qi)) pr = 0.f;
+                if (8 * (r >> 2) + (r & 3) > hi) pr = 0.f;
                 dsv[r] = pr * (dpacc[r] - dl);
             }
 #pragma unroll
