@@ -38,11 +38,19 @@
 //   Causal: key tiles past the workgroup's last query are never loaded, a
 //   wave skips the work of tiles past its own last query, and only tiles that
 //   straddle the diagonal (or the end of the sequence) apply the mask.
-//   Causal workgroups start with the longest query tiles.
-//   Block mask (one flag per 64 queries x 64 keys): each workgroup first lists
-//   the key tiles any of its four query blocks may see and runs the same
-//   phase schedule over that list only; a wave gives P = 0 to the listed
-//   tiles its own block may not see.
+//   Causal workgroups start with the longest query tiles.  Grids whose
+//   (head, query tile) items fill whole rounds of compute units run the
+//   persistent form below instead: one workgroup per compute unit over a
+//   fixed item list, the key/value stream running on across items.
+//   Sliding window (LOCAL): key tiles before every query's window are
+//   skipped like tiles past the diagonal, and the visible ones run in a
+//   rotated order so that query tiles that start together read each key
+//   tile they share at the same time, through the XCD's L2.
+//   Block mask (one flag per 64 queries x 64 keys): each wave group (two
+//   64-query blocks) first lists the key tiles either of its blocks may see,
+//   and streams that list through K/V buffers of its own in the same phase
+//   schedule; a wave gives P = 0 to the listed tiles its own block may not
+//   see, and skips their products when the next tile does not need them.
 #include <type_traits>
 
 #include "common.h"
