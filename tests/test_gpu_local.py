@@ -83,6 +83,34 @@ def test_window_one_returns_v():
     assert torch.equal(out, G.dev(v).repeat_interleave(2, dim=1))
 
 
+# The persistent window form at its edges, on a shape that takes it (whole
+# 256-query tiles, 32 heads x 8 tiles = one round of 256 compute units).  W = 1:
+# each query's one weight is exactly 1, so out = v bit for bit.  W >= S: the
+# window hides nothing, so the result is causal attention (compared with the
+# oracle, not with the causal kernel bit for bit: the persistent causal form
+# runs every other item's key tiles in descending order).
+PERSIST_EDGE = (1, 32, 8, 2048, 128)
+
+
+def test_persistent_window_one_returns_v():
+    B, Hq, Hkv, S, D = PERSIST_EDGE
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", seed=3102)
+    out, _ = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=True, window=1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, G.dev(v).repeat_interleave(Hq // Hkv, dim=1))
+
+
+@pytest.mark.parametrize("window", [2048, 100000])
+def test_persistent_wide_window_is_causal(orc, window):
+    B, Hq, Hkv, S, D = PERSIST_EDGE
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", seed=3103)
+    sc = 1.0 / math.sqrt(D)
+    out, lse = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=True, scale=sc, window=window)
+    torch.cuda.synchronize()
+    ref_o, ref_l = orc.attn_fwd(q.f32, k.f32, v.f32, sc, True)
+    G.check_close(f"local persistent {PERSIST_EDGE} W={window}", G.host(out), ref_o, "bf16", G.host(lse), ref_l)
+
+
 @pytest.mark.parametrize("window", [1024, 300])
 def test_c3_sampled(orc, window):
     c = inputs.CONFIGS["C3"]
