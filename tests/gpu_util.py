@@ -69,6 +69,21 @@ def check_grad(name, got, ref, tol=GRAD_TOL):
     assert rel_mean <= tol[1], f"{name}: mean err {rel_mean:.3e} of mean|ref| > {tol[1]}"
 
 
+def persistent_launch(B, Hq, S, causal) -> bool:
+    """Whether attn_fwd_bf16 takes the persistent schedule for this grid: one
+    workgroup per compute unit over whole rounds of units (causal: pairs of
+    query tiles), mirroring the launch code's choice."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nq = (S + 255) // 256
+    split = S > 256 and B * Hq * nq <= (256 if causal else 128)  # the key-split form
+    if split or S < 256 or (causal and nq % 2):
+        return False
+    units = B * Hq * (nq // 2 if causal else nq)
+    return units % cus == 0
+
+
 def dev(t, device="cuda"):
     import torch
 

@@ -207,18 +207,6 @@ def _stamped(dq, dk, dv, B, Hq, Hkv, S, D, sc, causal):
     return out, lse, rec[:n]
 
 
-def _persistent(B, Hq, S, causal):
-    """Whether the launch takes the persistent schedule: one workgroup per
-    compute unit over whole rounds of units (causal: pairs of query tiles)."""
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    nq = (S + 255) // 256
-    split = S > 256 and B * Hq * nq <= (256 if causal else 128)  # the key-split form
-    if split or S < 256 or (causal and nq % 2):
-        return False
-    units = B * Hq * (nq // 2 if causal else nq)
-    return units % cus == 0
-
-
 @pytest.mark.parametrize("name,causal", [("C3", True), ("C2", True), ("C3", False)])
 def test_stamped_launch(name, causal):
     """The stamped launch runs the same kernel: bit-identical results; every
@@ -234,7 +222,7 @@ def test_stamped_launch(name, causal):
     n = rec.shape[0]
     pairs = set(zip(rec[:, 6].tolist(), rec[:, 7].tolist()))
     assert len(pairs) == n
-    if _persistent(B, Hq, S, causal):
+    if G.persistent_launch(B, Hq, S, causal):
         assert n == torch.cuda.get_device_properties(0).multi_processor_count
     else:
         qt = (S + n // (B * Hq) - 1) // (n // (B * Hq))  # queries per workgroup
@@ -270,7 +258,7 @@ def test_persistent_schedule_full_compare(orc, shape):
     dq, dk, dv = G.dev(q), G.dev(k), G.dev(v)
     out, lse = api.fwd(dq, dk, dv, causal=causal, scale=sc)
     torch.cuda.synchronize()
-    assert _persistent(B, Hq, S, causal)
+    assert G.persistent_launch(B, Hq, S, causal)
     # the stamped launch shows the schedule taken: one record per compute unit
     out2, lse2, rec = _stamped(dq, dk, dv, B, Hq, Hkv, S, D, sc, causal)
     assert torch.equal(out, out2) and torch.equal(lse, lse2)

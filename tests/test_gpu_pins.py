@@ -46,8 +46,18 @@ ROUND = {"bf16": 2.0 ** -8, "f32": 2.0 ** -24}  # unit roundoff of the output ty
 # grid has at most 256 workgroups of 256 queries: the first and fourth shapes
 # (D = 128 and D = 64).  The second has S <= 256 (plain 256-query form on a
 # small grid); the third has more than 256 workgroups of 256 queries (the
-# 256-query kernel the benchmark times).
-SHAPES = [(1, 4, 2, 300, 128), (2, 2, 1, 129, 64), (2, 72, 8, 300, 128), (1, 2, 1, 300, 64)]
+# per-tile 256-query grid).  The fifth fills whole rounds of the 256 compute
+# units (256 causal pairs of query tiles, 512 tiles without the mask), so
+# the bf16 path takes the persistent form the benchmark times.
+SHAPES = [(1, 4, 2, 300, 128), (2, 2, 1, 129, 64), (2, 72, 8, 300, 128), (1, 2, 1, 300, 64),
+          (1, 64, 8, 2000, 128)]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_shapes_cover_the_persistent_form(causal):
+    """Only the fifth shape takes the persistent schedule."""
+    got = [G.persistent_launch(B, Hq, S, causal) for B, Hq, _, S, _ in SHAPES]
+    assert got == [False, False, False, False, True]
 
 
 def _prefix_mean(v64, causal):
