@@ -508,12 +508,18 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(Params p) {
     // redoes the exponentials, after which every p <= 1.
     auto softmax_impl = [&](int n0, auto may_mask) __attribute__((always_inline)) {
         if (may_mask && ((CAUSAL && n0 + BN - 1 > qwmin) || n0 + BN > S || (LOCAL && n0 <= qwmax - p.window))) {
+            // register r of key block sb holds key n0 + 4g + kofs, kofs =
+            // 32 sb + 8 (r / 4) + r % 4: masked when kofs passes hi (this
+            // lane's query, or S - 1) or, LOCAL, when kofs <= lo (a key
+            // before the row's window)
+            const int hi = (CAUSAL ? min(qi, S - 1) : S - 1) - (n0 + g * 4);
+            const int lo = LOCAL ? qi - p.window - (n0 + g * 4) : 0;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = n0 + sb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    if ((CAUSAL && key > qi) || key >= S || (LOCAL && key <= qi - p.window)) sacc[sb][r] = -INFINITY;
+                    const int kofs = sb * 32 + (r >> 2) * 8 + (r & 3);
+                    if (kofs > hi || (LOCAL && kofs <= lo)) sacc[sb][r] = -INFINITY;
                 }
             }
         }

@@ -263,13 +263,15 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Params p) {
     // softmax of tile n0 (from sacc)
     auto softmax = [&](int n0) __attribute__((always_inline)) {
         if ((CAUSAL && n0 + BN - 1 > qwmin) || n0 + BN > S) {
+            // register r of key block sb holds key n0 + 4g + kofs, kofs =
+            // 32 sb + 8 (r / 4) + r % 4: masked when kofs passes hi, the
+            // offset of this lane's last visible key (its query, or S - 1)
+            const int hi = (CAUSAL ? min(qi, S - 1) : S - 1) - (n0 + g * 4);
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = n0 + sb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    if ((CAUSAL && key > qi) || key >= S) sacc[sb][r] = -INFINITY;
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (sb * 32 + (r >> 2) * 8 + (r & 3) > hi) sacc[sb][r] = -INFINITY;
         }
         // lane max of the 32 scores: a chain of three-way maxima
         float tmax;
