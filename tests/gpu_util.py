@@ -6,7 +6,7 @@ import sys
 
 import numpy as np
 
-# spec tolerances: max-abs / mean-abs error of out against the fp64 oracle
+# the parity bar: max-abs / mean-abs error of out against the fp64 oracle
 TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}
 # lse is not bounded by the pages.  Every bf16 kernel whose lse is checked
 # here (fused forward, window and block masks, split-KV, the unfused softmax)
