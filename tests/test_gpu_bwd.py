@@ -82,6 +82,27 @@ def test_config_full(orc, name, causal):
     G.check_grad(f"{name} causal={causal} dv all rows", got[2], rdv)
 
 
+def test_long_sequence_sampled(orc):
+    """S = 16384 (256 query tiles of the dK/dV sweep per key tile, GQA group
+    2): dq on sampled query rows, dk and dv on sampled key rows (the oracle's
+    key pass needs the lse and delta of every query row: one row pass over
+    all of them)."""
+    B, Hq, Hkv, S, D = 1, 2, 1, 16384, 128
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", seed=2102)
+    do = inputs.make_dout(B, Hq, S, D, "bf16", seed=2102)
+    sc = 1.0 / math.sqrt(D)
+    dq, dk, dv = run_bwd(q, k, v, do, True, sc)
+    got_q, got_k, got_v = (G.host(t).reshape(-1, D) for t in (dq, dk, dv))
+    del dq, dk, dv
+    lse, delta, rdq = orc.attn_bwd_rows(q.f32, k.f32, v.f32, do.f32, sc, True)
+    rows = G.sample_rows(B, Hq, S, n_random=40, seed=2103, tile=128)
+    G.check_grad(f"S={S} dq rows={rows.size}", got_q[rows], rdq[rows])
+    keys = G.sample_rows(B, Hkv, S, n_random=40, seed=2104, tile=128)
+    rdk, rdv = orc.attn_bwd_keys(q.f32, k.f32, v.f32, do.f32, sc, True, lse, delta, keys=keys)
+    G.check_grad(f"S={S} dk keys={keys.size}", got_k[keys], rdk)
+    G.check_grad(f"S={S} dv keys={keys.size}", got_v[keys], rdv)
+
+
 def test_delta_workspace():
     """The workspace ends up holding delta_i = dout_i . out_i of the forward's out."""
     B, Hq, Hkv, S, D = 1, 2, 1, 150, 128
