@@ -111,6 +111,22 @@ def test_persistent_wide_window_is_causal(orc, window):
     G.check_close(f"local persistent {PERSIST_EDGE} W={window}", G.host(out), ref_o, "bf16", G.host(lse), ref_l)
 
 
+@pytest.mark.parametrize("window", [1024, 4000])
+def test_long_sequence_sampled(orc, window):
+    """S = 65536 (256 query workgroups per head, windows of 17 or 64 key
+    tiles in rotated order far from the sequence start) on sampled rows."""
+    B, Hq, Hkv, S, D = 1, 2, 1, 65536, 128
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", seed=3104)
+    sc = 1.0 / math.sqrt(D)
+    out, lse = api.fwd(G.dev(q), G.dev(k), G.dev(v), causal=True, scale=sc, window=window)
+    torch.cuda.synchronize()
+    rows = G.sample_rows(B, Hq, S, n_random=60, seed=3105, tile=256)
+    ref_o, ref_l = orc.attn_fwd_local(q.f32, k.f32, v.f32, sc, window, rows=rows)
+    idx = torch.from_numpy(rows).to(out.device)
+    G.check_close(f"S={S} local W={window} rows={rows.size}", G.host(out.view(-1, D)[idx]), ref_o, "bf16",
+                  G.host(lse.view(-1)[idx]), ref_l)
+
+
 @pytest.mark.parametrize("window", [1024, 300])
 def test_c3_sampled(orc, window):
     c = inputs.CONFIGS["C3"]
