@@ -6,16 +6,18 @@
 // matrix cores do not apply; it is a correctness path, sized for short
 // sequences, where the time is latency rather than arithmetic.
 //
-// Layout: a workgroup of eight waves owns QW queries (64 at D = 64, 32 at
-// D = 128).  Each lane holds 64 of its query's d's in registers, of q and of
-// the output accumulator (at D = 128 the two halves of a wave hold the two
-// halves of d and add their partial dot products with one lane swap).  The
-// eight waves (two per SIMD) split the key range: wave w takes the 16-key
-// steps n = w, w + 8, ..., each through its own K/V buffers in LDS (read as
-// 16-byte broadcasts), with the next step's tile loaded into registers while
-// the current one is used, so the loop has no workgroup barrier.  At the end
+// Layout: a workgroup of eight waves owns QW queries (16 at D = 64, 8 at
+// D = 128).  Each query takes DS = D / 16 adjacent lanes, each holding 16 of
+// its d's of q and of the output accumulator; a dot product is the lane's
+// 16-term partial sum plus DPP adds over the query's lanes (quad swaps, then
+// a half-row mirror at D = 128).  The eight waves (two per SIMD) split the
+// key range: wave w takes the 16-key steps n = w, w + 8, ..., each through
+// its own K/V buffers in LDS (a lane reads its 16 d's of a key as four
+// 16-byte reads), with the next step's tile loaded into registers while the
+// current one is used, so the loop has no workgroup barrier.  At the end
 // waves 1-7 hand (m, l, o) to wave 0 through LDS (over the K/V buffers),
-// which merges the eight partial softmaxes.
+// which merges the eight partial softmaxes.  Small query groups spread short
+// sequences over many compute units: a 128-query head takes 8 workgroups.
 #include "common.h"
 #include "launch.h"
 
@@ -24,6 +26,7 @@ namespace {
 
 constexpr int NWF = 8;   // waves per workgroup (split of the key range)
 constexpr int BNF = 16;  // keys per step
+constexpr int DLF = 16;  // d's per lane
 
 struct Params {
     const float* q;
@@ -37,17 +40,27 @@ struct Params {
 
 template <int D>
 struct F32Shape {
-    static constexpr int DS = D / 64;   // lanes per query
-    static constexpr int QW = 64 / DS;  // queries per workgroup
-    static constexpr int DL = D / DS;   // d's per lane (64)
-    static constexpr int TF = BNF * D;  // floats of one K or V step tile
+    static constexpr int DS = D / DLF;       // lanes per query
+    static constexpr int QW = 64 / DS;       // queries per workgroup
+    static constexpr int TF = BNF * D;       // floats of one K or V step tile
     static constexpr int LPT = TF / 64 / 4;  // 16-byte loads per lane per tile
 };
+
+// sum over the DS adjacent lanes of one query (DPP within rows of 16 lanes)
+template <int DS>
+__device__ __forceinline__ float query_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
+    if (DS == 8)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // half-row mirror
+    return x;
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * NWF) void fwd_f32_kernel(Params p) {
     using F = F32Shape<D>;
-    constexpr int DS = F::DS, QW = F::QW, DL = F::DL, TF = F::TF, LPT = F::LPT;
+    constexpr int DS = F::DS, QW = F::QW, DL = DLF, TF = F::TF, LPT = F::LPT;
+    static_assert(DS == 4 || DS == 8, "4 or 8 lanes per query");
     // per wave: K, V of its step; after the loop: o, m, l of waves 1..NWF-1
     constexpr int KVF = NWF * 2 * TF, REDF = (NWF - 1) * (DL + 2) * 64;
     __shared__ __attribute__((aligned(16))) float lds[KVF > REDF ? KVF : REDF];
@@ -64,8 +77,8 @@ __global__ __launch_bounds__(64 * NWF) void fwd_f32_kernel(Params p) {
     const int kvh = h / p.group;
     const int S = p.S;
     const int m0 = tile * QW;
-    const int qi = m0 + lane % QW;      // this lane's query
-    const int d0 = (lane / QW) * DL;    // its first d
+    const int qi = m0 + lane / DS;      // this lane's query
+    const int d0 = (lane % DS) * DL;    // its first d
     const int64_t row0 = (int64_t)bh * S;
     const int64_t kvrow0 = ((int64_t)b * p.Hkv + kvh) * S;
 
@@ -140,11 +153,7 @@ __global__ __launch_bounds__(64 * NWF) void fwd_f32_kernel(Params p) {
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                float x = dot[u];
-                if (DS == 2) {  // the other half of d, held by lane (lane + 32) % 64
-                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-                    x = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                }
+                const float x = query_sum<DS>(dot[u]);
                 const int key = n0 + j0 + u;
                 s[j0 + u] = ((CAUSAL && key > qi) || key >= S) ? -INFINITY : x;
                 mt = fmaxf(mt, s[j0 + u]);
