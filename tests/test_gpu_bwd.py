@@ -103,6 +103,34 @@ def test_long_sequence_sampled(orc):
     G.check_grad(f"S={S} dv keys={keys.size}", got_v[keys], rdv)
 
 
+# A closed form checked on the HIP path itself rather than against the
+# oracle: every row of P sums to 1, so for each key/value head
+#   sum_j dv_j = sum_j sum_i p_ij dout_i = sum_i dout_i
+# over the query heads of its group.  The kernels round p to bf16 before the
+# dV product and round dv to bf16 (a relative 2^-9 each), and p comes from
+# the forward's float32 lse (relative error far below 1e-4), so per (b, kv
+# head, d):  |sum_j dv_j - sum_i dout_i| <= 2^-8 (sum_i |dout_i| +
+# sum_j |dv_j|) + 1e-4 sum_i |dout_i|.  A gradient that drops a query head,
+# a masked key or the normalisation misses it by orders of magnitude.
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("shape", [(1, 4, 2, 700, 128), (2, 6, 2, 300, 64), (1, 2, 2, 2048, 128)],
+                         ids=lambda s: "B{}H{}kv{}S{}D{}".format(*s))
+def test_dv_sums_to_dout(shape, causal):
+    B, Hq, Hkv, S, D = shape
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, D, "bf16", seed=2105 + S)
+    do = inputs.make_dout(B, Hq, S, D, "bf16", seed=2105 + S)
+    _, _, dv = run_bwd(q, k, v, do, causal, 1.0 / math.sqrt(D))
+    g = Hq // Hkv
+    dv64 = G.host(dv)  # [B, Hkv, S, D]
+    do64 = do.f32.astype(np.float64).reshape(B, Hkv, g, S, D)
+    err = np.abs(dv64.sum(axis=2) - do64.sum(axis=(2, 3)))
+    ado = np.abs(do64).sum(axis=(2, 3))
+    bound = 2.0 ** -8 * (ado + np.abs(dv64).sum(axis=2)) + 1e-4 * ado
+    G.report(f"sum dv = sum dout {shape} causal={causal}", max_err=float(err.max()),
+             max_ratio=float((err / bound).max()))
+    assert np.all(err <= bound), f"max err {err.max():.3e}, bound {bound[err > bound].min():.3e}"
+
+
 def test_delta_workspace():
     """The workspace ends up holding delta_i = dout_i . out_i of the forward's out."""
     B, Hq, Hkv, S, D = 1, 2, 1, 150, 128
